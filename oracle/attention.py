@@ -1,0 +1,220 @@
+"""CPU oracle for exact softmax attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import or run anything in ``oracle/``.  The GPU library never
+calls it and shares no code with it; the seeded inputs both sides consume come
+from ``synth_inputs``, which holds no attention arithmetic.
+
+What it computes is the plain definition, in float64, with torch CPU ops used
+only as dense linear-algebra and elementwise primitives:
+
+    s_ij  = tau * q_i . k_j              for j in A(i)
+    LSE_i = ln sum_{j in A(i)} exp(s_ij) (computed as m_i + ln sum exp(s_ij - m_i))
+    P_ij  = exp(s_ij - LSE_i)  (0 outside A(i))
+    O_i   = sum_j P_ij v_j
+
+with A(i) = {0..N-1} (non-causal) or {0..i} (causal), and the textbook softmax
+Jacobian for the backward:
+
+    dP_ij = dO_i . v_j
+    c_i   = sum_k P_ik dP_ik
+    dS_ij = P_ij (dP_ij - c_i)
+    dQ_i  = tau * sum_j dS_ij k_j
+    dK_j  = tau * sum_i dS_ij q_i   (summed over the query heads of the group)
+    dV_j  = sum_i P_ij dO_i         (summed over the query heads of the group)
+
+Sources, by page title and section:
+  * [EVOL] "从“算力黑洞”到“效率革命”：大模型Attention的演进之路" (mhpn.cn):
+      §2 (标准Attention) gives Attention(Q,K,V) = softmax(QK^T / sqrt(d_k)) V;
+      §3 (MLA, i.e. multi-query) and its GQA paragraph give K/V head sharing
+      among groups of query heads; §6 (实战) gives ``is_causal=True`` as the
+      triangular mask that stops a position from seeing later positions.
+  * [LONGCTX] "6.1 2023 年代：長上下文擴展技術：FlashAttention、RoPE 與稀疏注意力"
+      (cccbook): §2.2 (分塊與重計算) -- the forward keeps the output and the
+      per-row log-sum-exp statistic; §2.3 -- the result is exact, identical to
+      standard softmax attention.
+  * [LA2] "Lightning Attention-2 新一代注意力机制": the mask of a
+      unidirectional (GPT-style) model is lower triangular.
+
+Readings where the pages leave a step open:
+  * the mask is additive minus infinity (masked probabilities are exactly 0);
+    the literal elementwise-product form on the [LA2] page would leave weight
+    on future keys, contradicting the "no future information" use in [EVOL] §6;
+  * causal alignment is j <= i with one sequence length for queries and keys,
+    so no row is ever fully masked;
+  * LSE is the natural log over the *scaled* scores, masked keys excluded;
+  * head h of the query reads K/V head floor(h / G), G = H_q / H_kv
+    (contiguous groups);
+  * the backward is the analytic derivative of the forward (the pages print no
+    gradient formulas) and uses the textbook c_i, not the rowsum(dO * O)
+    shortcut a fast kernel may take.
+
+Query rows are processed in blocks only to bound memory (a full 32K x 32K
+fp64 score matrix is 8 GiB); every row is materialised over all N keys with
+masked entries set to -inf, exactly as the naive three-pass method of [EVOL] §4
+would, just on the CPU.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "default_scale",
+    "attention_forward",
+    "attention_backward",
+    "attention_probs",
+    "forward_rows",
+    "backward_dq_rows",
+    "to_f64",
+]
+
+_ROW_BLOCK = 512
+
+
+def default_scale(d: int) -> float:
+    """tau = 1 / sqrt(d_k)  ([EVOL] §2)."""
+    return 1.0 / math.sqrt(d)
+
+
+def to_f64(x) -> torch.Tensor:
+    """Any array-like -> contiguous float64 CPU tensor."""
+    t = torch.as_tensor(x)
+    return t.to(device="cpu", dtype=torch.float64).contiguous()
+
+
+def _shapes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool):
+    """(B, H_q, H_kv, N_q, d, G).  Keys may number N_k != N_q only without a mask."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if causal and Nk != N:
+        raise ValueError("the causal mask needs as many keys as queries")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("H_q must be a multiple of H_kv")
+    return B, Hq, Hkv, N, d, Hq // Hkv
+
+
+def _row_probs(q_rows: torch.Tensor, k_head: torch.Tensor, rows: torch.Tensor,
+               causal: bool, scale: float) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Scores -> (P, LSE) for a set of query rows of one head, over all keys.
+
+    q_rows [R, d], k_head [N, d], rows [R] = the query positions i of q_rows.
+    Returns P [R, N] (exact zeros where masked) and LSE [R].
+    """
+    N = k_head.shape[0]
+    s = scale * (q_rows @ k_head.transpose(0, 1))              # s_ij, [R, N]
+    if causal:
+        keys = torch.arange(N, dtype=torch.int64)
+        s = s.masked_fill(keys[None, :] > rows[:, None], -math.inf)
+    m = s.max(dim=1).values                                    # finite: key 0 is always in A(i)
+    ell = torch.exp(s - m[:, None]).sum(dim=1)
+    lse = m + torch.log(ell)
+    p = torch.exp(s - lse[:, None])                            # exp(-inf) = 0 on masked keys
+    return p, lse
+
+
+def attention_forward(q, k, v, causal: bool, scale: Optional[float] = None,
+                      row_block: int = _ROW_BLOCK) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O [B,H_q,N,d] and LSE [B,H_q,N], both float64."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal)
+    tau = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for r0 in range(0, N, row_block):
+                r1 = min(N, r0 + row_block)
+                rows = torch.arange(r0, r1, dtype=torch.int64)
+                p, l_blk = _row_probs(q[b, h, r0:r1], k[b, g], rows, causal, tau)
+                o[b, h, r0:r1] = p @ v[b, g]
+                lse[b, h, r0:r1] = l_blk
+    return o, lse
+
+
+def attention_probs(q, k, causal: bool, scale: Optional[float] = None) -> torch.Tensor:
+    """The full probability matrix P [B,H_q,N_q,N_k] (small inputs only)."""
+    q, k = to_f64(q), to_f64(k)
+    B, Hq, Hkv, N, d, G = _shapes(q, k, k, causal)
+    tau = default_scale(d) if scale is None else float(scale)
+    out = torch.empty((B, Hq, N, k.shape[2]), dtype=torch.float64)
+    rows = torch.arange(N, dtype=torch.int64)
+    for b in range(B):
+        for h in range(Hq):
+            out[b, h], _ = _row_probs(q[b, h], k[b, h // G], rows, causal, tau)
+    return out
+
+
+def forward_rows(q, k, v, causal: bool, scale: Optional[float], b: int, h: int,
+                 rows: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O and LSE of selected query rows of one (batch, query head).
+
+    Used to check very large problems on sampled rows: each row is computed
+    from the definition over all N keys, independently of the other rows.
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = h // (Hq // Hkv)
+    d = q.shape[-1]
+    tau = default_scale(d) if scale is None else float(scale)
+    rows_t = torch.as_tensor(list(rows), dtype=torch.int64)
+    q_r = to_f64(q[b, h])[rows_t]
+    k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
+    p, lse = _row_probs(q_r, k_g, rows_t, causal, tau)
+    return p @ v_g, lse
+
+
+def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,
+                       row_block: int = _ROW_BLOCK):
+    """dQ [B,H_q,N,d], dK and dV [B,H_kv,N,d] of L = sum(dO * O), float64."""
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal)
+    if tuple(do.shape) != tuple(q.shape):
+        raise ValueError("dO must have the shape of Q")
+    tau = default_scale(d) if scale is None else float(scale)
+    dq = torch.zeros_like(q)
+    dk = torch.zeros_like(k)
+    dv = torch.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for r0 in range(0, N, row_block):
+                r1 = min(N, r0 + row_block)
+                rows = torch.arange(r0, r1, dtype=torch.int64)
+                q_blk, do_blk = q[b, h, r0:r1], do[b, h, r0:r1]
+                p, _ = _row_probs(q_blk, k[b, g], rows, causal, tau)
+                dp = do_blk @ v[b, g].transpose(0, 1)          # dP_ij = dO_i . v_j
+                c = (p * dp).sum(dim=1)                        # c_i = sum_k P_ik dP_ik
+                ds = p * (dp - c[:, None])                     # dS_ij
+                dq[b, h, r0:r1] = tau * (ds @ k[b, g])
+                dk[b, g] += tau * (ds.transpose(0, 1) @ q_blk)
+                dv[b, g] += p.transpose(0, 1) @ do_blk
+    return dq, dk, dv
+
+
+def backward_dq_rows(q, k, v, do, causal: bool, scale: Optional[float], b: int,
+                     h: int, rows: Sequence[int]) -> torch.Tensor:
+    """dQ of selected query rows of one (batch, query head).
+
+    dQ_i needs only row i of P and dP, so sampled rows of a large problem can
+    be checked one by one.
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = h // (Hq // Hkv)
+    d = q.shape[-1]
+    tau = default_scale(d) if scale is None else float(scale)
+    rows_t = torch.as_tensor(list(rows), dtype=torch.int64)
+    q_r = to_f64(q[b, h])[rows_t]
+    do_r = to_f64(do[b, h])[rows_t]
+    k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
+    p, _ = _row_probs(q_r, k_g, rows_t, causal, tau)
+    dp = do_r @ v_g.transpose(0, 1)
+    c = (p * dp).sum(dim=1)
+    ds = p * (dp - c[:, None])
+    return tau * (ds @ k_g)

@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs shared by the CPU oracle, the tests and the bench.
+
+This module holds no attention arithmetic: it only draws normal samples, scales
+them and rounds them to bfloat16.  Both the oracle and the GPU library consume
+the exact same bf16 values that come out of here, so a parity test compares the
+two implementations of one function on one input.
+
+Recipe (per workload, per seed):
+  * generator  ``numpy.random.Generator(numpy.random.PCG64(seed))``;
+  * draw order ``Q, K, V[, dO]``, each ``standard_normal(shape, dtype=float32)``
+    in C order over ``[B, H, N, d]`` (Q and dO use H = H_q, K and V use H_kv);
+  * multiply by the workload's input scale (1.0, or 0.5 -- exact in binary);
+  * round fp32 -> bf16 to nearest, ties to even, with integer bit operations.
+
+The bf16 payload is returned as ``uint16`` bit patterns; ``bf16_bits_to_f32``
+and ``bf16_bits_to_f64`` decode them exactly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "bf16_bits_to_f64",
+    "draw_normal_f32",
+    "make_inputs",
+    "make_custom_inputs",
+]
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention problem: shapes, input scale, seed and masking."""
+
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: Tuple[bool, ...]
+    seed: int
+    in_scale: float = 1.0
+    with_grad: bool = False
+    note: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def pairs(self, causal: bool) -> int:
+        """Unmasked (query, key) pairs over all (batch, query head)."""
+        per_head = self.N * (self.N + 1) // 2 if causal else self.N * self.N
+        return self.B * self.Hq * per_head
+
+    def fwd_flops(self, causal: bool) -> int:
+        """Algorithmic matmul FLOPs of the forward: 2d for QK^T plus 2d for PV."""
+        return 4 * self.d * self.pairs(causal)
+
+    def bwd_flops(self, causal: bool) -> int:
+        """Algorithmic matmul FLOPs of the backward: S, dP, dV, dQ and dK."""
+        return 10 * self.d * self.pairs(causal)
+
+
+# The five problems the benchmark and the parity suite are built around.
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in (
+        Workload("tiny", 1, 2, 2, 256, 64, (True, False), seed=0,
+                 note="fp32 N(0,1) draws; the GPU sees their bf16 rounding"),
+        Workload("fwd-2K", 4, 16, 16, 2048, 128, (True,), seed=1),
+        Workload("fwd-8K", 1, 32, 32, 8192, 128, (True,), seed=2, in_scale=0.5),
+        Workload("gqa-16K", 1, 64, 8, 16384, 128, (True,), seed=3),
+        Workload("fb-32K", 1, 8, 8, 32768, 128, (True,), seed=4, with_grad=True),
+    )
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest, ties to even); return uint16 bits.
+
+    Inputs are finite.  The rounding adds 0x7FFF plus the lowest kept bit to the
+    32-bit pattern and keeps the upper half, which is round-half-to-even on the
+    16 discarded bits.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns exactly to fp32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns exactly to fp64."""
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def draw_normal_f32(rng: np.random.Generator, shape, scale: float) -> np.ndarray:
+    x = rng.standard_normal(size=tuple(shape), dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    return x
+
+
+def make_custom_inputs(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int,
+                       in_scale: float = 1.0, with_grad: bool = False,
+                       keep_f32: bool = False) -> Dict[str, np.ndarray]:
+    """Draw Q, K, V (and dO) for an arbitrary shape with the recipe above.
+
+    Returns ``{"q","k","v"[,"do"]}`` as uint16 bf16 bit arrays; with
+    ``keep_f32`` also ``"q_f32"`` ... holding the unrounded fp32 draws.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shapes = {"q": (B, Hq, N, d), "k": (B, Hkv, N, d), "v": (B, Hkv, N, d)}
+    if with_grad:
+        shapes["do"] = (B, Hq, N, d)
+    out: Dict[str, np.ndarray] = {}
+    for name in ("q", "k", "v", "do"):
+        if name not in shapes:
+            continue
+        x = draw_normal_f32(rng, shapes[name], in_scale)
+        out[name] = f32_to_bf16_bits(x)
+        if keep_f32:
+            out[name + "_f32"] = x
+        del x
+    return out
+
+
+def make_inputs(workload: str | Workload, seed: Optional[int] = None,
+                keep_f32: bool = False) -> Dict[str, np.ndarray]:
+    """Inputs of a named workload (its own seed unless ``seed`` is given)."""
+    w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    return make_custom_inputs(w.B, w.Hq, w.Hkv, w.N, w.d,
+                              w.seed if seed is None else seed,
+                              in_scale=w.in_scale, with_grad=w.with_grad,
+                              keep_f32=keep_f32)

@@ -1,0 +1,73 @@
+"""The seeded input generator: bf16 rounding and reproducibility."""
+import numpy as np
+import pytest
+
+from synth_inputs import (WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits,
+                          make_custom_inputs, make_inputs)
+
+
+def f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("bits_in, bits_out", [
+    (0x3F800000, 0x3F80),   # 1.0 exact
+    (0x3F808000, 0x3F80),   # halfway, even kept (lower kept bit 0) -> down
+    (0x3F818000, 0x3F82),   # halfway, odd -> up to even
+    (0x3F808001, 0x3F81),   # just above halfway -> up
+    (0x3F807FFF, 0x3F80),   # just below halfway -> down
+    (0xBF818000, 0xBF82),   # sign symmetric
+    (0x80000000, 0x8000),   # -0 stays -0
+    (0x00000001, 0x0000),   # smallest subnormal rounds to +0
+    (0x00018000, 0x0002),   # subnormal halfway, odd -> up
+    (0x7F7FFFFF, 0x7F80),   # max float rounds up to +inf (RNE carries)
+    (0x7F7F7FFF, 0x7F7F),   # largest value that stays finite
+])
+def test_bf16_rne_bit_patterns(bits_in, bits_out):
+    assert int(f32_to_bf16_bits(f32(bits_in))[0]) == bits_out
+
+
+def test_bf16_round_trip_is_nearest():
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32)
+    b = f32_to_bf16_bits(x)
+    y = bf16_bits_to_f32(b)
+    # |x - y| <= half an ulp of bf16 (2^-8 relative to the binade)
+    ulp = np.ldexp(np.float32(1), np.frexp(np.abs(x))[1] - 8).astype(np.float32)
+    assert np.all(np.abs(x - y) <= ulp / 2)
+    # neighbours are never closer
+    up = bf16_bits_to_f32((b.astype(np.uint32) + 1).astype(np.uint16))
+    assert np.all(np.abs(x - y) <= np.abs(x - up))
+
+
+def test_reproducible_and_ordered():
+    a = make_custom_inputs(1, 2, 1, 64, 8, seed=7, with_grad=True)
+    b = make_custom_inputs(1, 2, 1, 64, 8, seed=7, with_grad=True)
+    for n in ("q", "k", "v", "do"):
+        assert np.array_equal(a[n], b[n])
+    c = make_custom_inputs(1, 2, 1, 64, 8, seed=8)
+    assert not np.array_equal(a["q"], c["q"])
+    # draw order: Q first, so Q does not depend on whether dO is drawn
+    assert np.array_equal(a["q"], c["q"]) is False
+    d = make_custom_inputs(1, 2, 1, 64, 8, seed=7, with_grad=False)
+    assert np.array_equal(a["q"], d["q"]) and np.array_equal(a["v"], d["v"])
+
+
+def test_workload_shapes_and_scale():
+    w = WORKLOADS["tiny"]
+    x = make_inputs(w, keep_f32=True)
+    assert x["q"].shape == (1, 2, 256, 64) and x["q"].dtype == np.uint16
+    assert np.array_equal(f32_to_bf16_bits(x["q_f32"]), x["q"])
+    assert WORKLOADS["gqa-16K"].group == 8
+    assert WORKLOADS["fwd-8K"].in_scale == 0.5
+    # 0.5 is applied before rounding: the bf16 values are exactly half of unit draws
+    half = make_custom_inputs(1, 1, 1, 32, 8, seed=2, in_scale=0.5)
+    unit = make_custom_inputs(1, 1, 1, 32, 8, seed=2, in_scale=1.0)
+    assert np.array_equal(bf16_bits_to_f32(half["k"]) * 2, bf16_bits_to_f32(unit["k"]))
+
+
+def test_flop_counts():
+    w = WORKLOADS["fwd-8K"]
+    assert w.pairs(True) == 32 * 8192 * 8193 // 2
+    assert w.fwd_flops(True) == 4 * 128 * w.pairs(True)
+    assert abs(w.fwd_flops(True) - 5.498e11) / 5.498e11 < 1e-3
+    assert WORKLOADS["fb-32K"].bwd_flops(True) == 10 * 128 * 8 * 32768 * 32769 // 2

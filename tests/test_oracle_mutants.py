@@ -1,0 +1,89 @@
+"""Planted mistakes in a copy of the oracle must be caught by its pins.
+
+Each mutant is the oracle's source with one plausible slip (a dropped term, a
+wrong sign, an off-by-one mask, a wrong head map, a missing scale, a swapped
+operand).  It is loaded as a separate module on the CPU; the real oracle is
+untouched.  The test passes when the pins used in ``test_oracle.py`` (brute
+force, the hand-worked examples) reject every mutant.
+"""
+import json
+import os
+import types
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bf_backward, bf_forward
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = open(os.path.join(ROOT, "oracle", "attention.py")).read()
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "hand_worked.json")))["cases"]
+
+MUTANTS = {
+    "dropped_scale": ("s = scale * (q_rows @ k_head.transpose(0, 1))", "s = (q_rows @ k_head.transpose(0, 1))"),
+    "mask_hides_diagonal": ("keys[None, :] > rows[:, None]", "keys[None, :] >= rows[:, None]"),
+    "mask_shows_next_key": ("keys[None, :] > rows[:, None]", "keys[None, :] > rows[:, None] + 1"),
+    "lse_drops_max": ("lse = m + torch.log(ell)", "lse = torch.log(ell)"),
+    "gqa_modulo_heads": ("            g = h // G\n            for r0 in range(0, N, row_block):\n                r1 = min(N, r0 + row_block)\n                rows = torch.arange(r0, r1, dtype=torch.int64)\n                p, l_blk",
+                         "            g = h % Hkv\n            for r0 in range(0, N, row_block):\n                r1 = min(N, r0 + row_block)\n                rows = torch.arange(r0, r1, dtype=torch.int64)\n                p, l_blk"),
+    "jacobian_sign": ("ds = p * (dp - c[:, None])                     # dS_ij", "ds = p * (dp + c[:, None])                     # dS_ij"),
+    "jacobian_drops_c": ("ds = p * (dp - c[:, None])                     # dS_ij", "ds = p * dp                     # dS_ij"),
+    "dk_no_scale": ("dk[b, g] += tau * (ds.transpose(0, 1) @ q_blk)", "dk[b, g] += (ds.transpose(0, 1) @ q_blk)"),
+    "dq_no_scale": ("dq[b, h, r0:r1] = tau * (ds @ k[b, g])", "dq[b, h, r0:r1] = (ds @ k[b, g])"),
+    "dv_uses_ds": ("dv[b, g] += p.transpose(0, 1) @ do_blk", "dv[b, g] += ds.transpose(0, 1) @ do_blk"),
+    "dp_uses_k": ("dp = do_blk @ v[b, g].transpose(0, 1)          # dP_ij", "dp = do_blk @ k[b, g].transpose(0, 1)          # dP_ij"),
+    "dk_overwrites_group": ("dk[b, g] += tau", "dk[b, g] = tau"),
+    "o_uses_k": ("o[b, h, r0:r1] = p @ v[b, g]", "o[b, h, r0:r1] = p @ k[b, g]"),
+}
+
+
+def load_mutant(name):
+    old, new = MUTANTS[name]
+    assert SRC.count(old) >= 1, f"mutation site for {name} not found"
+    src = SRC.replace(old, new, 1)
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src, f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def rnd(seed, *shape):
+    return torch.from_numpy(np.random.default_rng(seed).standard_normal(shape))
+
+
+def pins_pass(mod) -> bool:
+    """The brute-force and hand-worked pins, run against a candidate oracle."""
+    try:
+        for case in GOLDEN:
+            q, k, v, do = (torch.tensor(case[n], dtype=torch.float64) for n in ("q", "k", "v", "do"))
+            o, lse = mod.attention_forward(q, k, v, case["causal"], case["scale"])
+            grads = mod.attention_backward(q, k, v, do, case["causal"], case["scale"])
+            for got, n in zip((o, lse) + tuple(grads), ("o", "lse", "dq", "dk", "dv")):
+                if not torch.allclose(got, torch.tensor(case[n], dtype=torch.float64), atol=1e-12):
+                    return False
+        B, Hq, Hkv, N, d = 1, 4, 2, 9, 4
+        q, k, v, do = rnd(1, B, Hq, N, d), rnd(2, B, Hkv, N, d), rnd(3, B, Hkv, N, d), rnd(4, B, Hq, N, d)
+        for causal in (True, False):
+            o, lse = mod.attention_forward(q, k, v, causal, 0.37, row_block=4)
+            bo, bl = bf_forward(q, k, v, causal, 0.37)
+            if not (torch.allclose(o, torch.tensor(bo, dtype=torch.float64), atol=1e-11) and torch.allclose(lse, torch.tensor(bl, dtype=torch.float64), atol=1e-11)):
+                return False
+            g = mod.attention_backward(q, k, v, do, causal, 0.37, row_block=4)
+            bg = bf_backward(q, k, v, do, causal, 0.37)
+            for x, y in zip(g, bg):
+                if not torch.allclose(x, torch.tensor(y, dtype=torch.float64), atol=1e-10):
+                    return False
+    except Exception:
+        return False
+    return True
+
+
+def test_unmutated_copy_passes():
+    mod = types.ModuleType("oracle_copy")
+    exec(compile(SRC, "<oracle copy>", "exec"), mod.__dict__)
+    assert pins_pass(mod)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name):
+    assert not pins_pass(load_mutant(name)), f"pins did not catch mutant {name}"
