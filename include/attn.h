@@ -1,0 +1,129 @@
+/*
+ * attn.h -- C ABI of an IO-aware exact attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled dot-product attention
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * by tiling Q, K and V along the sequence: each block of query rows streams
+ * K/V tiles through on-chip memory while it keeps a running row maximum and
+ * row sum, so the N x N score matrix never reaches device memory.  The forward
+ * stores only O and the per-row log-sum-exp; the backward recomputes block
+ * scores from that log-sum-exp.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [EVOL]    "从“算力黑洞”到“效率革命”：大模型Attention的演进之路" (mhpn.cn)
+ *               §2  softmax(QK^T / sqrt(d_k)) V;
+ *               §3  multi-query / grouped-query heads sharing K and V;
+ *               §4  Flash Attention: tiling, online softmax statistics,
+ *                   recomputation in the backward, O(N) memory;
+ *               §6  the scaled_dot_product_attention call (query, key, value,
+ *                   is_causal) whose problem statement these entry points take;
+ *               §7  pitfall 1: a silent fallback to a slow path -- this
+ *                   library never falls back; it returns an error instead.
+ *   [LONGCTX] "6.1 2023 年代：長上下文擴展技術：FlashAttention、RoPE 與稀疏注意力"
+ *             (cccbook) §2.2 tiling plus recomputation, only O and the
+ *             log-sum-exp kept by the forward; §2.3 exact, not approximate.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, contiguous, row-major [B, H, N, d] (batch, heads,
+ *    sequence, head dim) -- the "(Batch, Heads, Seq_Len, Dim)" layout of
+ *    [EVOL] §6.  Q, O, dO, dQ have H = Hq heads; K, V, dK, dV have H = Hkv.
+ *  - bf16 tensors hold IEEE-style bfloat16 bit patterns (uint16 storage).
+ *    The log-sum-exp and the backward's workspace are fp32.
+ *  - Grouped heads: query head h reads K/V head h / (Hq / Hkv); Hkv = 1 is
+ *    multi-query attention, Hkv = Hq is plain multi-head attention.
+ *  - causal != 0 applies the lower-triangular mask: query i attends keys
+ *    j <= i (one sequence length N for queries and keys).
+ *  - scale multiplies the fp32 scores; the usual value is 1/sqrt(d).
+ *  - Every pointer is a device pointer (hipMalloc'd or a torch CUDA tensor),
+ *    16-byte aligned.  The caller allocates and owns every buffer, including
+ *    the workspace; the library allocates and frees nothing and keeps no
+ *    per-call state.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    Arguments are validated synchronously, before any HIP call; kernels are
+ *    then enqueued on the stream and the call returns without synchronising.
+ *    Outputs are valid once the stream has reached that point.
+ *  - Supported: d in {64, 128}, N >= 1 (any length, ragged tails included),
+ *    B, Hq, Hkv >= 1 with Hq % Hkv == 0, gfx950 devices only.
+ */
+#ifndef IO_AWARE_ATTN_H
+#define IO_AWARE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define ATTN_OK              0  /* success (work enqueued)                          */
+#define ATTN_ERR_NULL        1  /* a required pointer is NULL                       */
+#define ATTN_ERR_SHAPE       2  /* B, Hq, Hkv, N or d <= 0, Hq % Hkv != 0, or one
+                                   head's N*d elements would not fit in 2^31 - 1    */
+#define ATTN_ERR_UNSUPPORTED 3  /* d not in {64,128}, a pointer not 16-byte aligned,
+                                   or the current device is not gfx950              */
+#define ATTN_ERR_WORKSPACE   4  /* workspace smaller than attn_bwd_workspace_bytes  */
+#define ATTN_ERR_SCALE       5  /* scale not finite or not > 0                      */
+#define ATTN_ERR_HIP         6  /* a HIP runtime call or kernel launch failed; the
+                                   message is available from attn_strerror(6)       */
+
+/*
+ * Forward pass ([EVOL] §4, [LONGCTX] §2.2).
+ *   q    [B, Hq,  N, d] bf16, read
+ *   k, v [B, Hkv, N, d] bf16, read
+ *   o    [B, Hq,  N, d] bf16, written: softmax(scale*QK^T + mask) V, rounded
+ *        to nearest-even bf16
+ *   lse  [B, Hq,  N]    fp32, written: LSE_i = ln sum_{j visible} exp(scale*q_i.k_j),
+ *        natural log of the scaled scores, masked keys excluded
+ * o and lse must not alias the inputs.  Returns ATTN_OK or an error code; on
+ * an error nothing is enqueued and no output is touched.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+             void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for this problem: O(B*Hq*N), never
+ * O(N^2) ([EVOL] §4: memory goes from O(N^2) to O(N)).  Returns 0 when the
+ * arguments are invalid.
+ */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Backward pass with recomputation from the saved log-sum-exp ([LONGCTX] §2.2,
+ * [EVOL] §4): consumes only the inputs, the forward's O and LSE, and dO.
+ *   q, o, dout [B, Hq,  N, d] bf16, read (o and lse from attn_fwd with the
+ *                                  same inputs, causal flag and scale)
+ *   k, v       [B, Hkv, N, d] bf16, read
+ *   lse        [B, Hq,  N]    fp32, read
+ *   dq         [B, Hq,  N, d] bf16, written: dL/dQ for L = sum(dO * O)
+ *   dk, dv     [B, Hkv, N, d] bf16, written: dL/dK, dL/dV, summed over the
+ *                                  Hq/Hkv query heads that share each K/V head
+ *   workspace  device buffer of workspace_bytes >= attn_bwd_workspace_bytes();
+ *              its contents on entry are ignored and on exit are unspecified.
+ * Outputs must not alias inputs or each other.  Deterministic: the same
+ * inputs give bitwise the same outputs.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes,
+             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+             void* stream);
+
+/* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
+ * of the last failure on the calling thread.  Never NULL. */
+const char* attn_strerror(int code);
+
+/* ATTN_OK when device `device` exists and is a gfx950 part this library was
+ * built for; ATTN_ERR_UNSUPPORTED for another architecture; ATTN_ERR_HIP when
+ * the device cannot be queried.  ([EVOL] §7: check that the fast kernel is
+ * really the one that can run, instead of falling back.) */
+int attn_device_check(int device);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* IO_AWARE_ATTN_H */

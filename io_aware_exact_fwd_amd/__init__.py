@@ -1,0 +1,151 @@
+"""Python binding of the gfx950 attention library (``libattn.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI in ``include/attn.h``.  PyTorch provides device
+memory and the current stream; nothing here computes attention, and there is
+no CPU or PyTorch fallback -- a missing library or an unsupported device
+raises.
+
+    o, lse = fwd(q, k, v, causal=True)           # q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch  # loads the HIP runtime that libattn.so then binds to
+
+__all__ = [
+    "AttnError", "fwd", "bwd", "bwd_workspace_bytes", "device_check", "strerror",
+    "lib", "LIB_PATH", "EXPORTED",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_strerror",
+            "attn_device_check")
+
+ATTN_OK = 0
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: attn error {code}: {strerror(code)}")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libattn.so`` (built by ``io_aware_exact_fwd_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m io_aware_exact_fwd_amd.build` (no fallback exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_fwd.restype = i
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    L.attn_bwd.restype = i
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_strerror.argtypes = [i]
+    L.attn_strerror.restype = ctypes.c_char_p
+    L.attn_device_check.argtypes = [i]
+    L.attn_device_check.restype = i
+    _lib = L
+    return L
+
+
+def strerror(code: int) -> str:
+    return lib().attn_strerror(int(code)).decode()
+
+
+def device_check(device: int = 0) -> int:
+    return int(lib().attn_device_check(int(device)))
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Hkv: int, N: int, d: int) -> int:
+    return int(lib().attn_bwd_workspace_bytes(B, Hq, Hkv, N, d))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_bf16(name: str, t: torch.Tensor, shape) -> None:
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor) -> Tuple[int, int, int, int, int]:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    return B, Hq, k.shape[1], N, d
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+        lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O = softmax(scale*QK^T + mask)V (bf16) and LSE (fp32 [B,Hq,N]) on the GPU."""
+    B, Hq, Hkv, N, d = _dims(q, k)
+    _check_bf16("q", q, (B, Hq, N, d))
+    _check_bf16("k", k, (B, Hkv, N, d))
+    _check_bf16("v", v, (B, Hkv, N, d))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bf16("out", out, (B, Hq, N, d))
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                        B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd")
+    return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+        lse: torch.Tensor, do: torch.Tensor, causal: bool = True,
+        scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+        dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None,
+        stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV (bf16) of L = sum(dO * O), recomputing scores from the LSE."""
+    B, Hq, Hkv, N, d = _dims(q, k)
+    for name, t, shp in (("q", q, (B, Hq, N, d)), ("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
+                         ("o", o, (B, Hq, N, d)), ("do", do, (B, Hq, N, d))):
+        _check_bf16(name, t, shp)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd")
+    return dq, dk, dv

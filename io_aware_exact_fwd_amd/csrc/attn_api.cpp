@@ -1,0 +1,132 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h.
+//
+// Validation happens first and makes no HIP call, so every argument error
+// comes back before any device work and without a device present.  There is
+// no fallback path: an unsupported case is an error code, never a slower
+// kernel (page "从“算力黑洞”到“效率革命”：大模型Attention的演进之路", §7, pitfall 1:
+// a silent fallback to an inefficient implementation).
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "attn.h"
+#include "attn_launch.h"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_hip_msg[256] = "no HIP error recorded on this thread";
+
+int hip_fail(hipError_t e, const char* where) {
+  std::snprintf(g_hip_msg, sizeof g_hip_msg, "HIP error %d (%s) in %s", (int)e,
+                hipGetErrorString(e), where);
+  return ATTN_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_problem(int B, int Hq, int Hkv, int N, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if ((long long)N * d > INT_MAX) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * N > INT_MAX) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_scale(float scale) {
+  return (std::isfinite(scale) && scale > 0.f) ? ATTN_OK : ATTN_ERR_SCALE;
+}
+
+// Per-device architecture cache: 0 unknown, 1 gfx950, 2 something else.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int device_check_impl(int device) {
+  if (device < 0) return ATTN_ERR_UNSUPPORTED;
+  if (device < kMaxDevices) {
+    const int c = g_arch_ok[device].load(std::memory_order_relaxed);
+    if (c == 1) return ATTN_OK;
+    if (c == 2) return ATTN_ERR_UNSUPPORTED;
+  }
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device >= count) return ATTN_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (device < kMaxDevices) g_arch_ok[device].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+}
+
+int current_device_check() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return device_check_impl(dev);
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_problem(B, Hq, Hkv, N, d);
+  if (rc) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_UNSUPPORTED;
+  if ((rc = check_scale(scale))) return rc;
+  if ((rc = current_device_check())) return rc;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, scale};
+  hipError_t e = attn::launch_fwd(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd launch");
+}
+
+ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (check_problem(B, Hq, Hkv, N, d)) return 0;
+  return attn::bwd_workspace_bytes(B, Hq, N);
+}
+
+ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                         int N, int d, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return ATTN_ERR_NULL;
+  int rc = check_problem(B, Hq, Hkv, N, d);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes < attn::bwd_workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
+  if ((rc = check_scale(scale))) return rc;
+  if ((rc = current_device_check())) return rc;
+  attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace,
+                  B, Hq, Hkv, N, d, causal != 0, scale};
+  hipError_t e = attn::launch_bwd(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd launch");
+}
+
+ATTN_EXPORT const char* attn_strerror(int code) {
+  switch (code) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape: B, Hq, Hkv, N, d must be >= 1, Hq % Hkv == 0, N*d < 2^31";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported: d must be 64 or 128, pointers 16-byte aligned, device gfx950";
+    case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_SCALE: return "scale must be finite and > 0";
+    case ATTN_ERR_HIP: return g_hip_msg;
+    default: return "unknown attn error code";
+  }
+}
+
+ATTN_EXPORT int attn_device_check(int device) { return device_check_impl(device); }

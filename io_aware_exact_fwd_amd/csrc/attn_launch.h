@@ -1,0 +1,44 @@
+// attn_launch.h -- internal interface between the C ABI (attn_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: D_i = rowsum(dO * O), fp32 [B, Hq, N]
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;
+};
+
+// Bytes of workspace the backward uses (fp32 D per query row).
+inline size_t bwd_workspace_bytes(int B, int Hq, int N) {
+  return (size_t)B * Hq * N * sizeof(float);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,40 @@
+"""Helpers shared by the GPU parity tests (no attention arithmetic here)."""
+import sys
+
+import numpy as np
+import torch
+
+from synth_inputs import bf16_bits_to_f64
+
+# Tolerances of the parity bar: max |O_gpu - O_ref| <= 1e-2, max |LSE_gpu - LSE_ref|
+# <= 1e-3, and max |G_gpu - G_ref| / max |G_ref| <= 2e-2 for G in dQ, dK, dV.
+TOL_O = 1e-2
+TOL_LSE = 1e-3
+TOL_GRAD_REL = 2e-2
+
+
+def say(msg: str) -> None:
+    """Name the case about to run on the GPU, flushed, so a crash points at it."""
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bfloat16 CUDA tensor with the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def to_f64(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(bf16_bits_to_f64(bits))
+
+
+def dev_f64(t: torch.Tensor) -> torch.Tensor:
+    return t.detach().float().cpu().double()
+
+
+def max_abs(a: torch.Tensor, b: torch.Tensor) -> float:
+    return float((a - b).abs().max())
+
+
+def rel_maxnorm(a: torch.Tensor, b: torch.Tensor) -> float:
+    return float((a - b).abs().max() / b.abs().max().clamp_min(1e-30))

@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports what include/attn.h
+declares, and rejects bad arguments before it makes any HIP call.
+
+Pointers passed here are fake but aligned addresses; every call below fails
+validation before a pointer could be used.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import io_aware_exact_fwd_amd as attn
+    return attn.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+                                           "attn_strerror", "attn_device_check"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    import io_aware_exact_fwd_amd as attn
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(attn.EXPORTED) == set(declared_functions())
+
+
+def test_exports_nothing_else():
+    """Only the five C entry points are visible (the rest is hidden)."""
+    import subprocess
+    import io_aware_exact_fwd_amd as attn
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {s for s in syms if s.startswith("attn_")} == set(declared_functions())
+
+
+A = 0x10000           # aligned fake address
+MIS = 0x10008         # 8-byte aligned only
+
+
+def fwd(L, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=16, d=64, causal=1, scale=0.125):
+    return L.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, None)
+
+
+def bwd(L, ws_bytes=None, ws=A, B=1, Hq=2, Hkv=2, N=16, d=64, scale=0.125, **ptr):
+    p = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A)
+    p.update(ptr)
+    if ws_bytes is None:
+        ws_bytes = 1 << 20
+    return L.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                      ws, ws_bytes, B, Hq, Hkv, N, d, 1, scale, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_fwd_null(L, which):
+    assert fwd(L, **{which: None}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(Hq=0), dict(Hkv=0), dict(N=0), dict(N=-5), dict(d=0),
+                                dict(Hq=3, Hkv=2), dict(N=1 << 25, d=128)])
+def test_fwd_shape(L, kw):
+    assert fwd(L, **kw) == 2
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=256), dict(d=32), dict(q=MIS), dict(v=MIS), dict(lse=0x10004)])
+def test_fwd_unsupported(L, kw):
+    assert fwd(L, **kw) == 3
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("inf"), float("nan")])
+def test_fwd_scale(L, scale):
+    assert fwd(L, scale=scale) == 5
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"])
+def test_bwd_null(L, which):
+    assert bwd(L, **{which: None}) == 1
+    assert bwd(L, ws=None) == 1
+
+
+def test_bwd_workspace(L):
+    need = L.attn_bwd_workspace_bytes(2, 8, 2, 1000, 128)
+    assert need == 2 * 8 * 1000 * 4           # one fp32 per query row: O(N), not O(N^2)
+    assert bwd(L, B=2, Hq=8, Hkv=2, N=1000, d=128, ws_bytes=need - 1) == 4
+    assert L.attn_bwd_workspace_bytes(1, 3, 2, 10, 64) == 0      # invalid problem -> 0
+    assert L.attn_bwd_workspace_bytes(1, 8, 8, 32768, 128) == 8 * 32768 * 4
+
+
+def test_bwd_shape_and_scale(L):
+    assert bwd(L, Hq=4, Hkv=3) == 2
+    assert bwd(L, d=80) == 3
+    assert bwd(L, dk=MIS) == 3
+    assert bwd(L, scale=float("nan")) == 5
+
+
+def test_strerror(L):
+    for code in range(0, 7):
+        s = L.attn_strerror(code)
+        assert s and len(s) > 1
+    assert b"unknown" in L.attn_strerror(99)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_device_reports_hip_error(L):
+    """All arguments valid, no GPU: the device check fails with ATTN_ERR_HIP or
+    ATTN_ERR_UNSUPPORTED -- it never falls back to another path."""
+    rc = fwd(L)
+    assert rc in (3, 6)
+    assert L.attn_device_check(0) in (3, 6)
