@@ -37,6 +37,93 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K")
 
 
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
+CSRC = os.path.join(ROOT, "io_aware_exact_fwd_amd", "csrc")
+# source files each kernel is compiled from (their hash decides whether recorded
+# counters still describe the kernel)
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": ("attn_device.h", "attn_fwd.hip"),
+    "bwd_pre_kernel": ("attn_device.h", "attn_bwd.hip"),
+    "bwd_dkdv_kernel": ("attn_device.h", "attn_bwd.hip"),
+    "bwd_dq_kernel": ("attn_device.h", "attn_bwd.hip"),
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_sha(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _per_kernel(csv_path: str, counter: str):
+    """Average value of one counter per dispatch, by kernel short name."""
+    import csv
+    import collections
+    acc = collections.defaultdict(list)
+    with open(csv_path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            short = next((k for k in KERNEL_SOURCES if k in name), COPY_KERNEL if COPY_KERNEL in name else None)
+            if short:
+                acc[short].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str,
+                    mfma_csv: str | None = None) -> dict:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> profiles/counters.json.
+
+    Both counters are scaled by what they read for the plain copy of calib_mib
+    MiB that ran in the same process (it reads and writes calib_mib MiB).
+    """
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    kib = calib_mib * 1024.0
+    fs, ws = kib / fetch[COPY_KERNEL], kib / write[COPY_KERNEL]
+    out = {"workload": workload, "fetch_scale": fs, "write_scale": ws,
+           "calibration": f"one {calib_mib} MiB device copy ({COPY_KERNEL}) in the same process read "
+                          f"FETCH_SIZE={fetch[COPY_KERNEL]:.0f} KiB, WRITE_SIZE={write[COPY_KERNEL]:.0f} KiB",
+           "kernels": {}}
+    mfma = {}
+    if mfma_csv:
+        for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"):
+            mfma[c] = _per_kernel(mfma_csv, c)
+    for k in KERNEL_SOURCES:
+        if k not in fetch or k not in write:
+            continue
+        e = {"source_sha": source_sha(k), "fetch_kib": fetch[k], "write_kib": write[k],
+             "hbm_bytes": (fetch[k] * fs + write[k] * ws) * 1024.0}
+        if mfma and k in mfma["SQ_INSTS_VALU_MFMA_MOPS_BF16"]:
+            e["mfma_flop"] = mfma["SQ_INSTS_VALU_MFMA_MOPS_BF16"][k] * 512
+            e["mfma_busy_cycles"] = mfma["SQ_VALU_MFMA_BUSY_CYCLES"][k]
+            e["grbm_gui_active"] = mfma["GRBM_GUI_ACTIVE"][k]
+        out["kernels"][k] = e
+    os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
+    with open(COUNTERS_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from recorded counters, or None when the kernel's
+    sources changed since they were taken (or none were taken)."""
+    try:
+        with open(COUNTERS_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = rec.get("kernels", {}).get(kernel)
+    if rec.get("workload") != workload or not e or e.get("source_sha") != source_sha(kernel):
+        return None
+    return e["hbm_bytes"]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,6 +132,12 @@ def parse():
     ap.add_argument("--workload", default="fb-32K", choices=BENCH_WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle (for profiler runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before warm-up, so a "
+                         "counter run can scale FETCH_SIZE/WRITE_SIZE by a kernel of known traffic")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/counters.json from two rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--ingest-mfma", metavar="MFMA_CSV", default=None)
     ap.add_argument("--cpu-sample-heads", type=int, default=None,
                     help="query heads in the oracle's timed sample (default: sized for ~10-30 s)")
     return ap.parse_args()
@@ -85,6 +178,11 @@ def cpu_baseline(w, x, n_heads):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        rec = ingest_counters(args.ingest_counters[0], args.ingest_counters[1],
+                              args.copy_calibration_mib or 1024, args.workload, args.ingest_mfma)
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the library runs on one device; a multi-GPU split is not part of it)",
@@ -120,26 +218,43 @@ def main():
     if w.with_grad:
         do = dev(x["do"])
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(max(16, attn.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.N, w.d)),
-                         dtype=torch.uint8, device="cuda")
+        delta = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
+    # Each phase is one kernel launch; events between them give per-kernel
+    # durations on the stream the kernels run on.  The three backward phases
+    # are exactly what attn_bwd runs, in the same order.
+    phases = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if w.with_grad else [])
+
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        if w.with_grad:
-            attn.bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+        def mark(i):
             if ev is not None:
-                ev[2].record(stream)
+                ev[i].record(stream)
+        mark(0)
+        attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream)
+        mark(1)
+        if w.with_grad:
+            attn.bwd_preprocess(o, do, delta, stream=stream)
+            mark(2)
+            attn.bwd_dkdv(q, k, v, do, lse, delta, causal=True, dk=dk, dv=dv, stream=stream)
+            mark(3)
+            attn.bwd_dq(q, k, v, do, lse, delta, causal=True, dq=dq, stream=stream)
+            mark(4)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                     # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -147,31 +262,38 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events] if w.with_grad else []
     ms_per_step = wall * 1e3 / steps
+    pairs = w.pairs(True)
+    # algorithmic matmul FLOPs per unmasked pair, by kernel: the forward's QK^T
+    # and PV (4d); the dK/dV kernel's S, dP, dV and dK (8d); the dQ kernel's dQ
+    # (2d -- its S and dP are recomputation); the pre-pass does no matmul.
+    per_pair = {"fwd": 4 * w.d, "bwd_pre": 0, "bwd_dkdv": 8 * w.d, "bwd_dq": 2 * w.d}
+    kernel_name = {"fwd": "attn_fwd_kernel", "bwd_pre": "bwd_pre_kernel",
+                   "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
     fwd_flops = w.fwd_flops(True)
     bwd_flops = w.bwd_flops(True) if w.with_grad else 0
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    fwd_avg = float(np.mean(fwd_ms))
-    parts = {"fwd": {"ms_avg": fwd_avg, "ms_median": float(np.median(fwd_ms)),
-                     "tflops": fwd_flops / (fwd_avg * 1e-3) / 1e12}}
-    parts["fwd"]["pct_of_peak"] = 100 * parts["fwd"]["tflops"] / PEAK_BF16_TFLOPS
+    parts = {}
+    for i, ph in enumerate(phases):
+        ms = [e[i].elapsed_time(e[i + 1]) for e in events]
+        avg = float(np.mean(ms))
+        flops = per_pair[ph] * pairs
+        parts[ph] = {"kernel": kernel_name[ph], "ms_avg": avg, "ms_median": float(np.median(ms)),
+                     "algorithmic_flops": flops, "tflops": flops / (avg * 1e-3) / 1e12}
+        parts[ph]["pct_of_peak"] = 100 * parts[ph]["tflops"] / PEAK_BF16_TFLOPS
     if w.with_grad:
-        bwd_avg = float(np.mean(bwd_ms))
-        parts["bwd"] = {"ms_avg": bwd_avg, "ms_median": float(np.median(bwd_ms)),
-                        "tflops": bwd_flops / (bwd_avg * 1e-3) / 1e12}
-        parts["bwd"]["pct_of_peak"] = 100 * parts["bwd"]["tflops"] / PEAK_BF16_TFLOPS
+        bwd_ms = sum(parts[p]["ms_avg"] for p in phases[1:])
+        parts["bwd_total"] = {"ms_avg": bwd_ms, "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+                              "pct_of_peak": 100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
-    # the dominant launch: the forward kernel, or the backward call when it takes longer
-    dom = max(parts, key=lambda p: parts[p]["ms_avg"])
-    dom_flops = fwd_flops if dom == "fwd" else bwd_flops
-    achieved = dom_flops / (parts[dom]["ms_avg"] * 1e-3) / 1e12
+    dom = max(phases, key=lambda p: parts[p]["ms_avg"])
+    achieved = parts[dom]["tflops"]
+    traffic = recorded_traffic(kernel_name[dom], w.name)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "kernel": "attn_fwd_kernel" if dom == "fwd" else "attn_bwd (all backward kernels)"}
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel_name[dom],
+                "ms_per_launch": parts[dom]["ms_avg"], "algorithmic_flops_per_launch": parts[dom]["algorithmic_flops"]}
 
     result = {
         "metric": METRIC,

@@ -112,6 +112,29 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
              void* stream);
 
+/*
+ * The three stages attn_bwd runs, in this order, for callers that schedule
+ * them themselves -- for instance dK/dV and dQ on two streams, since both read
+ * only the inputs, the LSE and delta.  Same conventions and errors as attn_bwd.
+ *
+ * attn_bwd_preprocess: delta [B, Hq, N] fp32 (caller-owned, e.g. the first
+ *   B*Hq*N*4 bytes of attn_bwd's workspace) = rowsum(dO * O), which equals the
+ *   softmax-Jacobian term sum_k P_ik dP_ik of each query row.
+ * attn_bwd_dkdv: dK, dV [B, Hkv, N, d] bf16, each summed over the Hq/Hkv query
+ *   heads of its group, recomputing probabilities from lse ([LONGCTX] §2.2).
+ * attn_bwd_dq: dQ [B, Hq, N, d] bf16, recomputing probabilities from lse.
+ */
+int attn_bwd_preprocess(const void* o, const void* dout, float* delta,
+                        int B, int Hq, int N, int d, void* stream);
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                  const float* lse, const float* delta, void* dk, void* dv,
+                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                  void* stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, const float* delta, void* dq,
+                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                void* stream);
+
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
  * of the last failure on the calling thread.  Never NULL. */
 const char* attn_strerror(int code);

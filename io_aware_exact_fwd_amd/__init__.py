@@ -19,13 +19,13 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime that libattn.so then binds to
 
 __all__ = [
-    "AttnError", "fwd", "bwd", "bwd_workspace_bytes", "device_check", "strerror",
-    "lib", "LIB_PATH", "EXPORTED",
+    "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
+    "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
-EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_strerror",
-            "attn_device_check")
+EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_strerror", "attn_device_check")
 
 ATTN_OK = 0
 
@@ -53,6 +53,12 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.restype = i
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     L.attn_bwd.restype = i
+    L.attn_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+    L.attn_bwd_preprocess.restype = i
+    L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_bwd_dkdv.restype = i
+    L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_bwd_dq.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_strerror.argtypes = [i]
@@ -149,3 +155,64 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_bwd")
     return dq, dk, dv
+
+
+def _check_f32(name: str, t: torch.Tensor, shape) -> None:
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {tuple(shape)}")
+
+
+def bwd_preprocess(o: torch.Tensor, do: torch.Tensor, delta: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """delta [B,Hq,N] fp32 = rowsum(dO * O): the first stage of bwd."""
+    B, Hq, N, d = o.shape
+    _check_bf16("o", o, (B, Hq, N, d))
+    _check_bf16("do", do, (B, Hq, N, d))
+    if delta is None:
+        delta = torch.empty((B, Hq, N), dtype=torch.float32, device=o.device)
+    _check_f32("delta", delta, (B, Hq, N))
+    rc = lib().attn_bwd_preprocess(_ptr(o), _ptr(do), _ptr(delta), B, Hq, N, d, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_preprocess")
+    return delta
+
+
+def _stage_checks(q, k, v, do, lse, delta):
+    B, Hq, Hkv, N, d = _dims(q, k)
+    for name, t, shp in (("q", q, (B, Hq, N, d)), ("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
+                         ("do", do, (B, Hq, N, d))):
+        _check_bf16(name, t, shp)
+    _check_f32("lse", lse, (B, Hq, N))
+    _check_f32("delta", delta, (B, Hq, N))
+    return B, Hq, Hkv, N, d
+
+
+def bwd_dkdv(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[float] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """dK, dV (bf16) from the inputs, lse and delta: the second stage of bwd."""
+    B, Hq, Hkv, N, d = _stage_checks(q, k, v, do, lse, delta)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_bf16("dk", dk, (B, Hkv, N, d))
+    _check_bf16("dv", dv, (B, Hkv, N, d))
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dk),
+                             _ptr(dv), B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_dkdv")
+    return dk, dv
+
+
+def bwd_dq(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[float] = None,
+           dq: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dQ (bf16) from the inputs, lse and delta: the third stage of bwd."""
+    B, Hq, Hkv, N, d = _stage_checks(q, k, v, do, lse, delta)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check_bf16("dq", dq, (B, Hq, N, d))
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+                           B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_dq")
+    return dq

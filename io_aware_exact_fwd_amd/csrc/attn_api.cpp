@@ -116,6 +116,59 @@ ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd launch");
 }
 
+ATTN_EXPORT int attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq,
+                                    int N, int d, void* stream) {
+  if (!o || !dout || !delta) return ATTN_ERR_NULL;
+  int rc = check_problem(B, Hq, Hq, N, d);
+  if (rc) return rc;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta)) return ATTN_ERR_UNSUPPORTED;
+  if ((rc = current_device_check())) return rc;
+  attn::BwdArgs a{};
+  a.o = o;
+  a.dout = dout;
+  a.delta = delta;
+  a.B = B, a.Hq = Hq, a.Hkv = Hq, a.N = N, a.d = d;
+  hipError_t e = attn::launch_bwd_pre(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_preprocess launch");
+}
+
+// Shared checks of the two recomputing stages.
+static int check_stage(const void* q, const void* k, const void* v, const void* dout,
+                       const float* lse, const float* delta, const void* out1, const void* out2,
+                       int B, int Hq, int Hkv, int N, int d, float scale) {
+  if (!q || !k || !v || !dout || !lse || !delta || !out1 || !out2) return ATTN_ERR_NULL;
+  int rc = check_problem(B, Hq, Hkv, N, d);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, dout, lse, delta, out1, out2};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if ((rc = check_scale(scale))) return rc;
+  return current_device_check();
+}
+
+ATTN_EXPORT int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, const float* delta, void* dk, void* dv, int B,
+                              int Hq, int Hkv, int N, int d, int causal, float scale,
+                              void* stream) {
+  int rc = check_stage(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, N, d, scale);
+  if (rc) return rc;
+  attn::BwdArgs a{q, k, v, nullptr, lse, dout, nullptr, dk, dv, (float*)delta,
+                  B, Hq, Hkv, N, d, causal != 0, scale};
+  hipError_t e = attn::launch_bwd_dkdv(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_dkdv launch");
+}
+
+ATTN_EXPORT int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, const float* delta, void* dq, int B, int Hq,
+                            int Hkv, int N, int d, int causal, float scale, void* stream) {
+  int rc = check_stage(q, k, v, dout, lse, delta, dq, dq, B, Hq, Hkv, N, d, scale);
+  if (rc) return rc;
+  attn::BwdArgs a{q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, (float*)delta,
+                  B, Hq, Hkv, N, d, causal != 0, scale};
+  hipError_t e = attn::launch_bwd_dq(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_dq launch");
+}
+
 ATTN_EXPORT const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";

@@ -1,9 +1,446 @@
-// attn_bwd.hip -- backward pass (placeholder until the kernels land).
+// attn_bwd.hip -- backward pass with recomputation from the log-sum-exp, gfx950.
+//
+// Method (page "6.1 … 長上下文擴展技術：FlashAttention、RoPE 與稀疏注意力", §2.2;
+// page "从“算力黑洞”到“效率革命”：大模型Attention的演进之路", §4): the forward kept
+// only O and the per-row log-sum-exp; the backward recomputes each block of
+// probabilities from Q, K and that statistic instead of reading an N x N
+// matrix back, trading one extra multiply for a full HBM round trip.
+//
+// With L = sum(dO * O), P_ij = exp(tau q_i.k_j - LSE_i) on visible keys:
+//   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,
+//   dS_ij = P_ij (dP_ij - D_i) with D_i = dO_i . O_i (= sum_k P_ik dP_ik),
+//   dQ_i = tau sum_j dS_ij k_j,   dK_j = tau sum_i dS_ij q_i.
+//
+// Three kernels, in stream order, no atomics (bitwise deterministic):
+//   bwd_pre   D_i = rowsum(dO_i * O_i)                          (memory bound)
+//   bwd_dkdv  one workgroup per (batch, K/V head, 32*NW keys); each wave owns
+//             32 keys with dK^T and dV^T in fp32 registers and loops over the
+//             query tiles of every query head of the group, so grouped heads
+//             are summed without atomics;
+//   bwd_dq    one workgroup per (batch, query head, 32*NW queries); each wave
+//             owns 32 queries with dQ^T in registers and loops over key tiles.
+// Both main kernels use v_mfma_f32_32x32x16_bf16 and take the C layout of
+// one product straight back as the B operand of the next (see the forward).
 #include "attn_device.h"
 #include "attn_launch.h"
 
 namespace attn {
+namespace {
 
-hipError_t launch_bwd(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+// ---------------------------------------------------------------------------
+// D_i = sum_t dO[i,t] * O[i,t]   (fp32, one value per query row)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
+                                                      const uint16_t* __restrict__ dO,
+                                                      float* __restrict__ Dl, int rows) {
+  constexpr int TPR = D / 8;        // threads per row, 16 bytes each
+  constexpr int RPB = 256 / TPR;    // rows per block
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)(O + (size_t)row * D + c * 8);
+    const u32x4 b = *(const u32x4*)(dO + (size_t)row * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += bf16_lo(a[w]) * bf16_lo(b[w]) + bf16_hi(a[w]) * bf16_hi(b[w]);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && c == 0) Dl[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+struct DkdvCfg {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kBKV = NW * 32;   // keys per workgroup
+  static constexpr int kBQ = 64;         // query rows per LDS tile
+  using Stage = TileStager<D, kBQ, kThreads>;
+  // one LDS buffer: Q row-major, Q "4 rows per column", same for dO, then
+  // LSE*log2(e) and D for the tile's rows
+  static constexpr int kQrm = 0;
+  static constexpr int kQil = kQrm + Stage::kRowMajorBytes;
+  static constexpr int kOrm = kQil + Stage::kInterleavedBytes;
+  static constexpr int kOil = kOrm + Stage::kRowMajorBytes;
+  static constexpr int kLse = kOil + Stage::kInterleavedBytes;
+  static constexpr int kDel = kLse + kBQ * 4;
+  static constexpr int kBufBytes = kDel + kBQ * 4;
+  static constexpr int kLdsBytes = 2 * kBufBytes;
+};
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int Hq, int Hkv, int G,
+    int n_kb, float scale, float scale_log2) {
+  using C = DkdvCfg<D, NW>;
+  using Stage = typename C::Stage;
+  constexpr int NT = C::kThreads;
+  constexpr int BQ = C::kBQ;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int STRIDE = Stage::kRowStride;
+  constexpr int GB = Stage::kGroupBytes;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+
+  // heaviest key blocks (the first ones under the causal mask) first
+  const int bhk = blockIdx.x % (gridDim.x / n_kb);
+  const int kb = blockIdx.x / (gridDim.x / n_kb);
+  const int b = bhk / Hkv, hk = bhk - b * Hkv;
+  const int k0 = kb * C::kBKV;
+  const int kw0 = k0 + wave * 32;       // first key of this wave
+  const size_t kv_off = ((size_t)b * Hkv + hk) * N * D;
+
+  // this wave's K and V rows as B operands: lane holds row kw0 + l%32
+  u32x4 kf[DS], vf[DS];
+  {
+    const int key = kw0 + l32;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = key < N ? *(const u32x4*)(K + kv_off + (size_t)key * D + s * 16 + 8 * hi) : zero4();
+      vf[s] = key < N ? *(const u32x4*)(V + kv_off + (size_t)key * D + s * 16 + 8 * hi) : zero4();
+    }
+  }
+
+  f32x16 dkT[DB], dvT[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dkT[db] = f32x16{};
+    dvT[db] = f32x16{};
+  }
+
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;            // first query tile that sees these keys
+  const int per_head = n_qt - qt0;
+  const int n_iter = per_head * G;
+
+  Stage sq, sdo;
+  auto load_tile = [&](int it) {
+    const int hh = it / per_head, qt = qt0 + it % per_head;
+    const size_t qh = ((size_t)b * Hq + hk * G + hh);
+    sq.load(Q + qh * N * D, qt * BQ, N, tid);
+    sdo.load(dO + qh * N * D, qt * BQ, N, tid);
+  };
+  float lse_reg = 0.f, del_reg = 0.f;
+  auto load_stats = [&](int it) {
+    const int hh = it / per_head, qt = qt0 + it % per_head;
+    const size_t qh = ((size_t)b * Hq + hk * G + hh);
+    const int row = qt * BQ + (tid & (BQ - 1));
+    if (tid < 2 * BQ) {
+      if (tid < BQ) lse_reg = row < N ? LSE[qh * N + row] * kLog2e : INFINITY;  // rows >= N: P = 0
+      else del_reg = row < N ? Dl[qh * N + row] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* base = smem + buf * C::kBufBytes;
+    sq.template store<true, true>(base + C::kQrm, base + C::kQil, tid);
+    sdo.template store<true, true>(base + C::kOrm, base + C::kOil, tid);
+    if (tid < BQ) ((float*)(base + C::kLse))[tid] = lse_reg;
+    else if (tid < 2 * BQ) ((float*)(base + C::kDel))[tid - BQ] = del_reg;
+  };
+
+  if (n_iter > 0) {
+    load_tile(0);
+    load_stats(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < n_iter) {
+      load_tile(it + 1);
+      load_stats(it + 1);
+    }
+    const int q0 = (qt0 + it % per_head) * BQ;
+    const unsigned char* base = smem + buf * C::kBufBytes;
+    const float* lse_l = (const float*)(base + C::kLse);
+    const float* del_l = (const float*)(base + C::kDel);
+
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      const int qs = q0 + qb * 32;
+      if (kw0 >= N || (CAUSAL && qs + 31 < kw0)) continue;   // nothing visible for this wave
+
+      // S = Q K^T and dP = dO V^T: 32 queries x 32 keys, lane holds key column l%32
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int sl = 0; sl < DS; ++sl) {
+        s = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kQrm, qb * 32, sl, l32, hi), kf[sl], s);
+        dp = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kOrm, qb * 32, sl, l32, hi), vf[sl], dp);
+      }
+
+      // P = 2^(s*tau*log2e - LSE*log2e), dS = P (dP - D); rows 8r + 4hi + 0..3
+      const bool need_mask = CAUSAL && qs < kw0 + 31;
+      const int key = kw0 + l32;
+      float p[16], ds[16];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4 lv = *(const f32x4*)(lse_l + qb * 32 + 8 * r + 4 * hi);
+        const f32x4 dv = *(const f32x4*)(del_l + qb * 32 + 8 * r + 4 * hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * r + e;
+          float pv = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lv[e]));
+          if (need_mask && key > qs + 8 * r + 4 * hi + e) pv = 0.f;
+          p[i] = pv;
+          ds[i] = pv * (dp[i] - dv[e]);
+        }
+      }
+
+      // dV^T += dO^T P and dK^T += Q^T dS: k slots of slab h2 are query rows
+      // 16*h2 + {4hi..4hi+3, 8+4hi..8+4hi+3} of this 32-row block
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4 pb = pack8(p + 8 * h2);
+        const u32x4 dsb = pack8(ds + 8 * h2);
+        const int g0 = qb * 8 + h2 * 4 + hi;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dvT[db] = mfma_32x32x16(lds_tr_frag<GB>(base + C::kOil, g0, db * 32 + l32), pb, dvT[db]);
+          dkT[db] = mfma_32x32x16(lds_tr_frag<GB>(base + C::kQil, g0, db * 32 + l32), dsb, dkT[db]);
+        }
+      }
+    }
+
+    if (it + 1 < n_iter) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds key kw0 + l%32, d rows db*32 + 8r + 4hi + 0..3
+  const int key = kw0 + l32;
+  if (key < N) {
+    uint16_t* dkr = dK + kv_off + (size_t)key * D;
+    uint16_t* dvr = dV + kv_off + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = db * 32 + 8 * r + 4 * hi;
+        *(u32x2*)(dkr + d0) = u32x2{pack_bf16x2(dkT[db][4 * r] * scale, dkT[db][4 * r + 1] * scale),
+                                    pack_bf16x2(dkT[db][4 * r + 2] * scale, dkT[db][4 * r + 3] * scale)};
+        *(u32x2*)(dvr + d0) = u32x2{pack_bf16x2(dvT[db][4 * r], dvT[db][4 * r + 1]),
+                                    pack_bf16x2(dvT[db][4 * r + 2], dvT[db][4 * r + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ
+// ---------------------------------------------------------------------------
+template <int D, int NW>
+struct DqCfg {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kBQ = NW * 32;    // query rows per workgroup
+  static constexpr int kBC = 64;         // keys per LDS tile
+  using Stage = TileStager<D, kBC, kThreads>;
+  static constexpr int kKrm = 0;
+  static constexpr int kKil = kKrm + Stage::kRowMajorBytes;
+  static constexpr int kVrm = kKil + Stage::kInterleavedBytes;
+  static constexpr int kBufBytes = kVrm + Stage::kRowMajorBytes;
+  static constexpr int kLdsBytes = 2 * kBufBytes;
+};
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
+    float scale_log2, int xcd_remap) {
+  using C = DqCfg<D, NW>;
+  using Stage = typename C::Stage;
+  constexpr int NT = C::kThreads;
+  constexpr int BC = C::kBC;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int KB = BC / 32;
+  constexpr int STRIDE = Stage::kRowStride;
+  constexpr int GB = Stage::kGroupBytes;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+
+  int bh, qrank;
+  const int w = blockIdx.x;
+  if (xcd_remap) {
+    const int hx = BH >> 3;
+    const int i = w >> 3;
+    bh = (w & 7) * hx + (i % hx);
+    qrank = i / hx;
+  } else {
+    bh = w % BH;
+    qrank = w / BH;
+  }
+  const int qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
+  const int b = bh / Hq, h = bh - b * Hq, hk = h / G;
+  const size_t q_off = (size_t)bh * N * D;
+  const size_t kv_off = ((size_t)b * Hkv + hk) * N * D;
+  const int q0 = qb * C::kBQ;
+  const int qw0 = q0 + wave * 32;
+  const int q = qw0 + l32;              // this lane's query row
+  const bool wave_live = qw0 < N;
+
+  u32x4 qf[DS], dof[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    qf[s] = q < N ? *(const u32x4*)(Q + q_off + (size_t)q * D + s * 16 + 8 * hi) : zero4();
+    dof[s] = q < N ? *(const u32x4*)(dO + q_off + (size_t)q * D + s * 16 + 8 * hi) : zero4();
+  }
+  const float lse_l2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
+  const float del = q < N ? Dl[(size_t)bh * N + q] : 0.f;
+
+  f32x16 dqT[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqT[db] = f32x16{};
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  Stage sk, sv;
+  auto store_tile = [&](int buf) {
+    unsigned char* base = smem + buf * C::kBufBytes;
+    sk.template store<true, true>(base + C::kKrm, base + C::kKil, tid);
+    sv.template store<true, false>(base + C::kVrm, nullptr, tid);
+  };
+  sk.load(K + kv_off, 0, N, tid);
+  sv.load(V + kv_off, 0, N, tid);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    const int kstart = j * BC;
+    if (j + 1 < n_tiles) {
+      sk.load(K + kv_off, kstart + BC, N, tid);
+      sv.load(V + kv_off, kstart + BC, N, tid);
+    }
+    if (wave_live && (!CAUSAL || kstart <= qw0 + 31)) {
+      const unsigned char* base = smem + buf * C::kBufBytes;
+      const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0);
+#pragma unroll
+      for (int x = 0; x < KB; ++x) {
+        // S^T and dP^T: 32 keys x 32 queries, lane holds query column l%32
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int sl = 0; sl < DS; ++sl) {
+          s = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kKrm, x * 32, sl, l32, hi), qf[sl], s);
+          dp = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kVrm, x * 32, sl, l32, hi), dof[sl], dp);
+        }
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float pv = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lse_l2));
+          if (need_mask) {
+            const int key = kstart + x * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (key >= N || (CAUSAL && key > q)) pv = 0.f;
+          }
+          ds[i] = pv * (dp[i] - del);
+        }
+        // dQ^T += K^T dS^T: k slots of slab h2 are keys 16*h2 + {4hi.., 8+4hi..}
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const u32x4 dsb = pack8(ds + 8 * h2);
+          const int g0 = x * 8 + h2 * 4 + hi;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            dqT[db] = mfma_32x32x16(lds_tr_frag<GB>(base + C::kKil, g0, db * 32 + l32), dsb, dqT[db]);
+        }
+      }
+    }
+    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (q < N) {
+    uint16_t* dqr = dQ + q_off + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = db * 32 + 8 * r + 4 * hi;
+        *(u32x2*)(dqr + d0) = u32x2{pack_bf16x2(dqT[db][4 * r] * scale, dqT[db][4 * r + 1] * scale),
+                                    pack_bf16x2(dqT[db][4 * r + 2] * scale, dqT[db][4 * r + 3] * scale)};
+      }
+  }
+}
+
+template <typename KernelT>
+hipError_t allow_lds(KernelT kern, int bytes) {
+  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D>
+hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
+  const int rows = a.B * a.Hq * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, stream,
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+  return hipGetLastError();
+}
+
+constexpr int kNwKV = 4, kNwQ = 4;
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {
+  using CK = DkdvCfg<D, kNwKV>;
+  auto kern = bwd_dkdv_kernel<D, kNwKV, CAUSAL>;
+  static const hipError_t attr = allow_lds(kern, CK::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
+  const long long grid = (long long)a.B * a.Hkv * n_kb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), CK::kLdsBytes, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                     a.N, a.Hq, a.Hkv, a.Hq / a.Hkv, n_kb, a.scale, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
+  using CQ = DqCfg<D, kNwQ>;
+  auto kern = bwd_dq_kernel<D, kNwQ, CAUSAL>;
+  static const hipError_t attr = allow_lds(kern, CQ::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
+  const int BH = a.B * a.Hq;
+  const long long grid = (long long)BH * n_qb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CQ::kThreads), CQ::kLdsBytes, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, BH, a.Hq,
+                     a.Hkv, a.Hq / a.Hkv, n_qb, a.scale, a.scale * kLog2e, BH % 8 == 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 128 ? launch_pre_t<128>(a, stream) : launch_pre_t<64>(a, stream);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128)
+    return a.causal ? launch_dkdv_t<128, true>(a, stream) : launch_dkdv_t<128, false>(a, stream);
+  return a.causal ? launch_dkdv_t<64, true>(a, stream) : launch_dkdv_t<64, false>(a, stream);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128)
+    return a.causal ? launch_dq_t<128, true>(a, stream) : launch_dq_t<128, false>(a, stream);
+  return a.causal ? launch_dq_t<64, true>(a, stream) : launch_dq_t<64, false>(a, stream);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  hipError_t e = launch_bwd_pre(a, stream);
+  if (e == hipSuccess) e = launch_bwd_dkdv(a, stream);
+  if (e == hipSuccess) e = launch_bwd_dq(a, stream);
+  return e;
+}
 
 }  // namespace attn

@@ -51,8 +51,17 @@ struct FwdCfg {
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
-template <int D, int QG, int BC, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
+// Rescaling of the running output.  The reference maximum a row's
+// exponentials are taken against moves when a tile's maximum exceeds it by
+// more than LAG (log2 units); the multiply of the accumulator is skipped
+// whenever no row of the wave moved.  LAG = 0 keeps the exact running max, so
+// the largest probability of a row is exactly 1 and rounds to bf16 without
+// error (this matters for peaked rows).  LAG > 0 gives the same quotient
+// sum 2^(s-m) v / sum 2^(s-m) with factors bounded by 2^LAG, and skips most
+// rescales, at the cost of rounding that largest term too.
+template <int D, int QG, int BC, int NW, int WPE, bool CAUSAL, int LAG = 0>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale_log2, int xcd_remap) {
@@ -228,11 +237,19 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
         for (int x = 0; x < KB; ++x)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[x][g][i]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run[g], mx * scale_log2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2_fast(m_run[g] - m_use);
-        m_run[g] = m_new;
+        mx = fmaxf(mx, swap_halves(mx)) * scale_log2;
+        // move the reference maximum only when it falls more than LAG behind
+        const bool move = mx > m_run[g] + (float)LAG;
+        if (__any(move)) {
+          const float m_new = move ? mx : m_run[g];
+          const float alpha = exp2_fast(m_run[g] - m_new);   // 0 on the first tile
+          m_run[g] = m_new;
+          l_run[g] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db][g] *= alpha;
+        }
+        // m_run is finite from the first visited tile on: key 0 is visible to every row
+        const float m_use = m_run[g];
         float lsum = 0.f;
 #pragma unroll
         for (int x = 0; x < KB; ++x) {
@@ -249,9 +266,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
                                  pack_bf16x2(p[8 * h2 + 4], p[8 * h2 + 5]),
                                  pack_bf16x2(p[8 * h2 + 6], p[8 * h2 + 7])};
         }
-        l_run[g] = l_run[g] * alpha + lsum;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db][g] *= alpha;
+        l_run[g] += lsum;
       }
 
       // O^T[db][g] += V^T P^T: slab h2 of key block x holds keys
@@ -300,14 +315,14 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(
   }
 }
 
-template <int D, int QG, int BC, int NW, bool CAUSAL>
+template <int D, int QG, int BC, int NW, int WPE, bool CAUSAL, int LAG = 0>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, QG, BC, NW>;
   const int n_qb = (a.N + C::kBR - 1) / C::kBR;
   const int BH = a.B * a.Hq;
   const long long grid = (long long)BH * n_qb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  auto kern = attn_fwd_kernel<D, QG, BC, NW, CAUSAL>;
+  auto kern = attn_fwd_kernel<D, QG, BC, NW, WPE, CAUSAL, LAG>;
   // more than 64 KB of dynamic LDS has to be allowed once per kernel instance
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
@@ -323,12 +338,15 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  constexpr int QG = 1, BC = 64, NW = 4;
+  // 8 waves x 32 rows = 256 query rows per workgroup, 128-key tiles (135 KB
+  // of double-buffered LDS: one workgroup per CU), two waves per SIMD (<= 256
+  // registers each) so one wave's softmax VALU work overlaps the other's MFMAs.
+  constexpr int QG = 1, BC = 128, NW = 8, WPE = 2;
   if (a.d == 128)
-    return a.causal ? launch_fwd_t<128, QG, BC, NW, true>(a, stream)
-                    : launch_fwd_t<128, QG, BC, NW, false>(a, stream);
-  return a.causal ? launch_fwd_t<64, QG, BC, NW, true>(a, stream)
-                  : launch_fwd_t<64, QG, BC, NW, false>(a, stream);
+    return a.causal ? launch_fwd_t<128, QG, BC, NW, WPE, true>(a, stream)
+                    : launch_fwd_t<128, QG, BC, NW, WPE, false>(a, stream);
+  return a.causal ? launch_fwd_t<64, QG, BC, NW, WPE, true>(a, stream)
+                  : launch_fwd_t<64, QG, BC, NW, WPE, false>(a, stream);
 }
 
 }  // namespace attn

@@ -39,6 +39,11 @@ inline size_t bwd_workspace_bytes(int B, int Hq, int N) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// The backward's stages; launch_bwd runs all three in order.  Each reads the
+// BwdArgs fields it needs (delta must be set for all of them).
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -36,5 +36,12 @@ def max_abs(a: torch.Tensor, b: torch.Tensor) -> float:
     return float((a - b).abs().max())
 
 
-def rel_maxnorm(a: torch.Tensor, b: torch.Tensor) -> float:
-    return float((a - b).abs().max() / b.abs().max().clamp_min(1e-30))
+def rel_maxnorm(a: torch.Tensor, b: torch.Tensor, floor: float = 0.0) -> float:
+    """max |a - b| / max |b|, the denominator floored at ``floor``.
+
+    A gradient that is exactly zero in the mathematics (dQ and dK when every
+    row sees a single key) has max |b| = 0; the floor -- 1e-3 times the largest
+    gradient of the same problem -- keeps the ratio meaningful there and is
+    far below max |b| in every other case.
+    """
+    return float((a - b).abs().max() / max(float(b.abs().max()), floor, 1e-30))

@@ -29,6 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
+                                           "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
                                            "attn_strerror", "attn_device_check"])
 
 
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_exports_nothing_else():
-    """Only the five C entry points are visible (the rest is hidden)."""
+    """Only the declared C entry points are visible (the rest is hidden)."""
     import subprocess
     import io_aware_exact_fwd_amd as attn
     out = subprocess.run(["nm", "-D", "--defined-only", attn.LIB_PATH], capture_output=True, text=True).stdout
@@ -105,6 +106,20 @@ def test_bwd_shape_and_scale(L):
     assert bwd(L, d=80) == 3
     assert bwd(L, dk=MIS) == 3
     assert bwd(L, scale=float("nan")) == 5
+
+
+def test_stage_argument_errors(L):
+    assert L.attn_bwd_preprocess(None, A, A, 1, 2, 16, 64, None) == 1
+    assert L.attn_bwd_preprocess(A, A, A, 1, 2, 16, 96, None) == 3
+    assert L.attn_bwd_preprocess(A, A, A, 1, 0, 16, 64, None) == 2
+    assert L.attn_bwd_preprocess(A, MIS, A, 1, 2, 16, 64, None) == 3
+    args = [A] * 8
+    assert L.attn_bwd_dkdv(*args, 1, 4, 3, 16, 128, 1, 0.1, None) == 2
+    assert L.attn_bwd_dkdv(*args[:6], None, A, 1, 4, 2, 16, 128, 1, 0.1, None) == 1
+    assert L.attn_bwd_dkdv(*args, 1, 4, 2, 16, 128, 1, -0.1, None) == 5
+    assert L.attn_bwd_dq(*args[:7], 1, 4, 2, 16, 128, 1, float("inf"), None) == 5
+    assert L.attn_bwd_dq(*args[:6], MIS, 1, 4, 2, 16, 128, 1, 0.1, None) == 3
+    assert L.attn_bwd_dq(A, A, A, A, None, A, A, 1, 4, 2, 16, 128, 1, 0.1, None) == 1
 
 
 def test_strerror(L):
