@@ -42,10 +42,10 @@ CSRC = os.path.join(ROOT, "io_aware_exact_fwd_amd", "csrc")
 # source files each kernel is compiled from (their hash decides whether recorded
 # counters still describe the kernel)
 KERNEL_SOURCES = {
-    "attn_fwd_kernel": ("attn_device.h", "attn_fwd.hip"),
-    "bwd_pre_kernel": ("attn_device.h", "attn_bwd.hip"),
-    "bwd_dkdv_kernel": ("attn_device.h", "attn_bwd.hip"),
-    "bwd_dq_kernel": ("attn_device.h", "attn_bwd.hip"),
+    "attn_fwd_kernel": ("attn_device.h", "attn_layout.h", "attn_fwd.hip"),
+    "bwd_pre_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
+    "bwd_dkdv_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
+    "bwd_dq_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 

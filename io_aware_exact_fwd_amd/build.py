@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
-HEADERS = ["attn_device.h", "attn_launch.h"]
+HEADERS = ["attn_device.h", "attn_launch.h", "attn_layout.h"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",

@@ -13,14 +13,19 @@
 //
 // Three kernels, in stream order, no atomics (bitwise deterministic):
 //   bwd_pre   D_i = rowsum(dO_i * O_i)                          (memory bound)
-//   bwd_dkdv  one workgroup per (batch, K/V head, 32*NW keys); each wave owns
-//             32 keys with dK^T and dV^T in fp32 registers and loops over the
-//             query tiles of every query head of the group, so grouped heads
-//             are summed without atomics;
+//   bwd_dkdv  one workgroup per (batch, K/V head, 32*NWK keys): the key block's
+//             K and V stay in LDS; 2*NWK waves = NWK key groups of 32 x two
+//             halves of each 64-row query tile, each wave with dK^T and dV^T
+//             in fp32 registers; the loop runs over the query tiles of every
+//             query head of the group, so grouped heads are summed without
+//             atomics; the two halves' partial sums are added through LDS at
+//             the end;
 //   bwd_dq    one workgroup per (batch, query head, 32*NW queries); each wave
 //             owns 32 queries with dQ^T in registers and loops over key tiles.
-// Both main kernels use v_mfma_f32_32x32x16_bf16 and take the C layout of
-// one product straight back as the B operand of the next (see the forward).
+// All tiles move global -> LDS by 16-byte direct loads into the swizzled
+// layout of attn_layout.h; operands are row fragments or transposing LDS
+// reads.  The C layout of one product goes straight back as the B operand of
+// the next (see the forward).  Both main kernels run two waves per SIMD.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -53,60 +58,99 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
 // ---------------------------------------------------------------------------
 // dK, dV
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NWK>
 struct DkdvCfg {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kBKV = NW * 32;   // keys per workgroup
-  static constexpr int kBQ = 64;         // query rows per LDS tile
-  using Stage = TileStager<D, kBQ, kThreads>;
-  // one LDS buffer: Q row-major, Q "4 rows per column", same for dO, then
-  // LSE*log2(e) and D for the tile's rows
-  static constexpr int kQrm = 0;
-  static constexpr int kQil = kQrm + Stage::kRowMajorBytes;
-  static constexpr int kOrm = kQil + Stage::kInterleavedBytes;
-  static constexpr int kOil = kOrm + Stage::kRowMajorBytes;
-  static constexpr int kLse = kOil + Stage::kInterleavedBytes;
-  static constexpr int kDel = kLse + kBQ * 4;
-  static constexpr int kBufBytes = kDel + kBQ * 4;
-  static constexpr int kLdsBytes = 2 * kBufBytes;
+  static constexpr int kNW = 2 * NWK;             // waves: NWK key groups x 2 query halves
+  static constexpr int kThreads = kNW * 64;
+  static constexpr int kBKV = NWK * 32;           // keys per workgroup
+  static constexpr int kBQ = 64;                  // query rows per tile
+  static constexpr int kKVTile = kBKV * 2 * D;    // bytes of the K (or V) block
+  static constexpr int kQTile = kBQ * 2 * D;      // bytes of a Q (or dO) tile
+  // LDS: K | V | (Q, dO) buffer 0 | (Q, dO) buffer 1 | (lse, delta) x 2
+  static constexpr int kK = 0;
+  static constexpr int kV = kKVTile;
+  static constexpr int kQBuf = 2 * kKVTile;
+  static constexpr int kStats = kQBuf + 2 * 2 * kQTile;
+  static constexpr int kLdsBytes = kStats + 2 * 2 * kBQ * 4;
+  // the second query half's dK^T, dV^T, parked for the final reduction
+  static constexpr int kRedBytes = NWK * 2 * (D / 32) * 16 * 64 * 4;
+  static_assert(kRedBytes <= kLdsBytes, "reduction fits in the tile memory");
 };
 
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+template <int D, int NWK, int WPE, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64),
+                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int Hq, int Hkv, int G,
-    int n_kb, float scale, float scale_log2) {
-  using C = DkdvCfg<D, NW>;
-  using Stage = typename C::Stage;
-  constexpr int NT = C::kThreads;
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
+    float scale, float scale_log2, int xcd_remap) {
+  using C = DkdvCfg<D, NWK>;
+  constexpr int NW = C::kNW;
   constexpr int BQ = C::kBQ;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int STRIDE = Stage::kRowStride;
-  constexpr int GB = Stage::kGroupBytes;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int kg = wave % NWK;      // key group: keys kw0 .. kw0+31
+  const int qh = wave / NWK;      // query half: rows 32*qh .. 32*qh+31 of each tile
 
-  // heaviest key blocks (the first ones under the causal mask) first
-  const int bhk = blockIdx.x % (gridDim.x / n_kb);
-  const int kb = blockIdx.x / (gridDim.x / n_kb);
+  // heaviest key blocks (the first ones under the causal mask) first; when
+  // B*Hkv is a multiple of 8 all key blocks of one K/V head share an XCD, so
+  // the Q/dO tiles they all read stay in that XCD's L2
+  int bhk, kb;
+  const int w = blockIdx.x;
+  if (xcd_remap) {
+    const int hx = BHkv >> 3;
+    const int i = w >> 3;
+    bhk = (w & 7) * hx + (i % hx);
+    kb = i / hx;
+  } else {
+    bhk = w % BHkv;
+    kb = w / BHkv;
+  }
   const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const int k0 = kb * C::kBKV;
-  const int kw0 = k0 + wave * 32;       // first key of this wave
+  const int kw0 = k0 + kg * 32;
   const size_t kv_off = ((size_t)b * Hkv + hk) * N * D;
 
-  // this wave's K and V rows as B operands: lane holds row kw0 + l%32
-  u32x4 kf[DS], vf[DS];
-  {
-    const int key = kw0 + l32;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      kf[s] = key < N ? *(const u32x4*)(K + kv_off + (size_t)key * D + s * 16 + 8 * hi) : zero4();
-      vf[s] = key < N ? *(const u32x4*)(V + kv_off + (size_t)key * D + s * 16 + 8 * hi) : zero4();
+  unsigned char* Kt = smem + C::kK;
+  unsigned char* Vt = smem + C::kV;
+  auto qtile = [&](int buf) { return smem + C::kQBuf + buf * 2 * C::kQTile; };
+  auto stats = [&](int buf) { return (float*)(smem + C::kStats + buf * 2 * BQ * 4); };
+
+  const int n_qt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;            // first query tile that sees these keys
+  const int per_head = n_qt - qt0;
+  const int n_iter = per_head * G;
+
+  auto issue = [&](int it, int buf) {
+    const int hh = it / per_head, qt = qt0 + it % per_head;
+    const size_t qh_off = ((size_t)b * Hq + hk * G + hh) * N * D;
+    direct_tile_load<D, BQ, NW>(Q + qh_off, qt * BQ, N, qtile(buf), wave, lane);
+    direct_tile_load<D, BQ, NW>(dO + qh_off, qt * BQ, N, qtile(buf) + C::kQTile, wave, lane);
+  };
+  float stat_reg = 0.f;   // threads 0..63: LSE*log2(e) of a row; 64..127: its D
+  auto load_stats = [&](int it) {
+    if (tid < 2 * BQ) {
+      const int hh = it / per_head, qt = qt0 + it % per_head;
+      const int row = qt * BQ + (tid & (BQ - 1));
+      const size_t idx = ((size_t)b * Hq + hk * G + hh) * N + row;
+      if (tid < BQ) stat_reg = row < N ? LSE[idx] * kLog2e : INFINITY;   // rows >= N: P = 0
+      else stat_reg = row < N ? Dl[idx] : 0.f;
     }
-  }
+  };
+  auto store_stats = [&](int buf) {
+    if (tid < 2 * BQ) stats(buf)[tid] = stat_reg;
+  };
+
+  direct_tile_load<D, C::kBKV, NW>(K + kv_off, k0, N, Kt, wave, lane);
+  direct_tile_load<D, C::kBKV, NW>(V + kv_off, k0, N, Vt, wave, lane);
+  issue(0, 0);
+  load_stats(0);
+  store_stats(0);
+  wait_all_memory();
+  __syncthreads();
 
   f32x16 dkT[DB], dvT[DB];
 #pragma unroll
@@ -115,65 +159,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     dvT[db] = f32x16{};
   }
 
-  const int n_qt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? k0 / BQ : 0;            // first query tile that sees these keys
-  const int per_head = n_qt - qt0;
-  const int n_iter = per_head * G;
-
-  Stage sq, sdo;
-  auto load_tile = [&](int it) {
-    const int hh = it / per_head, qt = qt0 + it % per_head;
-    const size_t qh = ((size_t)b * Hq + hk * G + hh);
-    sq.load(Q + qh * N * D, qt * BQ, N, tid);
-    sdo.load(dO + qh * N * D, qt * BQ, N, tid);
-  };
-  float lse_reg = 0.f, del_reg = 0.f;
-  auto load_stats = [&](int it) {
-    const int hh = it / per_head, qt = qt0 + it % per_head;
-    const size_t qh = ((size_t)b * Hq + hk * G + hh);
-    const int row = qt * BQ + (tid & (BQ - 1));
-    if (tid < 2 * BQ) {
-      if (tid < BQ) lse_reg = row < N ? LSE[qh * N + row] * kLog2e : INFINITY;  // rows >= N: P = 0
-      else del_reg = row < N ? Dl[qh * N + row] : 0.f;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    unsigned char* base = smem + buf * C::kBufBytes;
-    sq.template store<true, true>(base + C::kQrm, base + C::kQil, tid);
-    sdo.template store<true, true>(base + C::kOrm, base + C::kOil, tid);
-    if (tid < BQ) ((float*)(base + C::kLse))[tid] = lse_reg;
-    else if (tid < 2 * BQ) ((float*)(base + C::kDel))[tid - BQ] = del_reg;
-  };
-
-  if (n_iter > 0) {
-    load_tile(0);
-    load_stats(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
   for (int it = 0; it < n_iter; ++it) {
     const int buf = it & 1;
     if (it + 1 < n_iter) {
-      load_tile(it + 1);
+      issue(it + 1, buf ^ 1);
       load_stats(it + 1);
     }
-    const int q0 = (qt0 + it % per_head) * BQ;
-    const unsigned char* base = smem + buf * C::kBufBytes;
-    const float* lse_l = (const float*)(base + C::kLse);
-    const float* del_l = (const float*)(base + C::kDel);
-
-#pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      const int qs = q0 + qb * 32;
-      if (kw0 >= N || (CAUSAL && qs + 31 < kw0)) continue;   // nothing visible for this wave
+    const int qs = (qt0 + it % per_head) * BQ + 32 * qh;   // first query row of this wave
+    if (kw0 < N && !(CAUSAL && qs + 31 < kw0)) {
+      const unsigned char* Qt = qtile(buf);
+      const unsigned char* dOt = Qt + C::kQTile;
+      const float* lse_l = stats(buf);
+      const float* del_l = lse_l + BQ;
 
       // S = Q K^T and dP = dO V^T: 32 queries x 32 keys, lane holds key column l%32
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int sl = 0; sl < DS; ++sl) {
-        s = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kQrm, qb * 32, sl, l32, hi), kf[sl], s);
-        dp = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kOrm, qb * 32, sl, l32, hi), vf[sl], dp);
+        s = mfma_32x32x16(row_frag<D>(Qt, lane, 32 * qh, sl), row_frag<D>(Kt, lane, 32 * kg, sl), s);
+        dp = mfma_32x32x16(row_frag<D>(dOt, lane, 32 * qh, sl), row_frag<D>(Vt, lane, 32 * kg, sl), dp);
       }
 
       // P = 2^(s*tau*log2e - LSE*log2e), dS = P (dP - D); rows 8r + 4hi + 0..3
@@ -182,8 +186,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
       float p[16], ds[16];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const f32x4 lv = *(const f32x4*)(lse_l + qb * 32 + 8 * r + 4 * hi);
-        const f32x4 dv = *(const f32x4*)(del_l + qb * 32 + 8 * r + 4 * hi);
+        const f32x4 lv = *(const f32x4*)(lse_l + 32 * qh + 8 * r + 4 * hi);
+        const f32x4 dv = *(const f32x4*)(del_l + 32 * qh + 8 * r + 4 * hi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
@@ -195,23 +199,38 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
       }
 
       // dV^T += dO^T P and dK^T += Q^T dS: k slots of slab h2 are query rows
-      // 16*h2 + {4hi..4hi+3, 8+4hi..8+4hi+3} of this 32-row block
+      // 16*h2 + {4hi..4hi+3, 8+4hi..8+4hi+3} of this wave's 32 rows
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const u32x4 pb = pack8(p + 8 * h2);
         const u32x4 dsb = pack8(ds + 8 * h2);
-        const int g0 = qb * 8 + h2 * 4 + hi;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dvT[db] = mfma_32x32x16(lds_tr_frag<GB>(base + C::kOil, g0, db * 32 + l32), pb, dvT[db]);
-          dkT[db] = mfma_32x32x16(lds_tr_frag<GB>(base + C::kQil, g0, db * 32 + l32), dsb, dkT[db]);
+          dvT[db] = mfma_32x32x16(tr_frag<D>(dOt, lane, 32 * qh + 16 * h2, db * 32), pb, dvT[db]);
+          dkT[db] = mfma_32x32x16(tr_frag<D>(Qt, lane, 32 * qh + 16 * h2, db * 32), dsb, dkT[db]);
         }
       }
     }
 
-    if (it + 1 < n_iter) store_tile(buf ^ 1);
+    if (it + 1 < n_iter) store_stats(buf ^ 1);
+    wait_all_memory();
     __syncthreads();
   }
+
+  // add the second query half's partial sums to the first half's
+  float* red = (float*)smem;
+  auto red_at = [&](int t, int db, int i) { return red + ((((kg * 2 + t) * DB + db) * 16 + i) * 64 + lane); };
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        *red_at(0, db, i) = dkT[db][i];
+        *red_at(1, db, i) = dvT[db][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 1) return;
 
   // epilogue: lane holds key kw0 + l%32, d rows db*32 + 8r + 4hi + 0..3
   const int key = kw0 + l32;
@@ -219,51 +238,47 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     uint16_t* dkr = dK + kv_off + (size_t)key * D;
     uint16_t* dvr = dV + kv_off + (size_t)key * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+      f32x16 a = dkT[db], v = dvT[db];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        a[i] = (a[i] + *red_at(0, db, i)) * scale;
+        v[i] += *red_at(1, db, i);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d0 = db * 32 + 8 * r + 4 * hi;
-        *(u32x2*)(dkr + d0) = u32x2{pack_bf16x2(dkT[db][4 * r] * scale, dkT[db][4 * r + 1] * scale),
-                                    pack_bf16x2(dkT[db][4 * r + 2] * scale, dkT[db][4 * r + 3] * scale)};
-        *(u32x2*)(dvr + d0) = u32x2{pack_bf16x2(dvT[db][4 * r], dvT[db][4 * r + 1]),
-                                    pack_bf16x2(dvT[db][4 * r + 2], dvT[db][4 * r + 3])};
+        *(u32x2*)(dkr + d0) = u32x2{pack_bf16x2(a[4 * r], a[4 * r + 1]), pack_bf16x2(a[4 * r + 2], a[4 * r + 3])};
+        *(u32x2*)(dvr + d0) = u32x2{pack_bf16x2(v[4 * r], v[4 * r + 1]), pack_bf16x2(v[4 * r + 2], v[4 * r + 3])};
       }
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int BC, int NW>
 struct DqCfg {
   static constexpr int kThreads = NW * 64;
-  static constexpr int kBQ = NW * 32;    // query rows per workgroup
-  static constexpr int kBC = 64;         // keys per LDS tile
-  using Stage = TileStager<D, kBC, kThreads>;
-  static constexpr int kKrm = 0;
-  static constexpr int kKil = kKrm + Stage::kRowMajorBytes;
-  static constexpr int kVrm = kKil + Stage::kInterleavedBytes;
-  static constexpr int kBufBytes = kVrm + Stage::kRowMajorBytes;
-  static constexpr int kLdsBytes = 2 * kBufBytes;
+  static constexpr int kBQ = NW * 32;               // query rows per workgroup
+  static constexpr int kTile = BC * 2 * D;          // bytes of one K or V tile
+  static constexpr int kLdsBytes = 2 * 2 * kTile;   // double-buffered K and V
 };
 
-template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
+template <int D, int BC, int NW, int WPE, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
     float scale_log2, int xcd_remap) {
-  using C = DqCfg<D, NW>;
-  using Stage = typename C::Stage;
-  constexpr int NT = C::kThreads;
-  constexpr int BC = C::kBC;
+  using C = DqCfg<D, BC, NW>;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KB = BC / 32;
-  constexpr int STRIDE = Stage::kRowStride;
-  constexpr int GB = Stage::kGroupBytes;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
   int bh, qrank;
@@ -301,26 +316,22 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
-  Stage sk, sv;
-  auto store_tile = [&](int buf) {
-    unsigned char* base = smem + buf * C::kBufBytes;
-    sk.template store<true, true>(base + C::kKrm, base + C::kKil, tid);
-    sv.template store<true, false>(base + C::kVrm, nullptr, tid);
+  auto issue_tile = [&](int j, int buf) {
+    unsigned char* kt = smem + buf * 2 * C::kTile;
+    direct_tile_load<D, BC, NW>(K + kv_off, j * BC, N, kt, wave, lane);
+    direct_tile_load<D, BC, NW>(V + kv_off, j * BC, N, kt + C::kTile, wave, lane);
   };
-  sk.load(K + kv_off, 0, N, tid);
-  sv.load(V + kv_off, 0, N, tid);
-  store_tile(0);
+  issue_tile(0, 0);
+  wait_all_memory();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int kstart = j * BC;
-    if (j + 1 < n_tiles) {
-      sk.load(K + kv_off, kstart + BC, N, tid);
-      sv.load(V + kv_off, kstart + BC, N, tid);
-    }
+    if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
     if (wave_live && (!CAUSAL || kstart <= qw0 + 31)) {
-      const unsigned char* base = smem + buf * C::kBufBytes;
+      const unsigned char* kt = smem + buf * 2 * C::kTile;
+      const unsigned char* vt = kt + C::kTile;
       const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0);
 #pragma unroll
       for (int x = 0; x < KB; ++x) {
@@ -328,8 +339,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int sl = 0; sl < DS; ++sl) {
-          s = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kKrm, x * 32, sl, l32, hi), qf[sl], s);
-          dp = mfma_32x32x16(lds_row_frag<STRIDE>(base + C::kVrm, x * 32, sl, l32, hi), dof[sl], dp);
+          s = mfma_32x32x16(row_frag<D>(kt, lane, x * 32, sl), qf[sl], s);
+          dp = mfma_32x32x16(row_frag<D>(vt, lane, x * 32, sl), dof[sl], dp);
         }
         float ds[16];
 #pragma unroll
@@ -345,14 +356,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const u32x4 dsb = pack8(ds + 8 * h2);
-          const int g0 = x * 8 + h2 * 4 + hi;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            dqT[db] = mfma_32x32x16(lds_tr_frag<GB>(base + C::kKil, g0, db * 32 + l32), dsb, dqT[db]);
+            dqT[db] = mfma_32x32x16(tr_frag<D>(kt, lane, x * 32 + 16 * h2, db * 32), dsb, dqT[db]);
         }
       }
     }
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    wait_all_memory();
     __syncthreads();
   }
 
@@ -383,28 +393,33 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int kNwKV = 4, kNwQ = 4;
+// dK/dV: 4 key groups x 2 query halves = 8 waves, 128 keys per workgroup.
+constexpr int kDkdvNWK = 4, kDkdvWPE = 2;
+// dQ: 8 waves x 32 queries, 64-key tiles.
+constexpr int kDqBC = 64, kDqNW = 8, kDqWPE = 2;
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {
-  using CK = DkdvCfg<D, kNwKV>;
-  auto kern = bwd_dkdv_kernel<D, kNwKV, CAUSAL>;
+  using CK = DkdvCfg<D, kDkdvNWK>;
+  auto kern = bwd_dkdv_kernel<D, kDkdvNWK, kDkdvWPE, CAUSAL>;
   static const hipError_t attr = allow_lds(kern, CK::kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
-  const long long grid = (long long)a.B * a.Hkv * n_kb;
+  const int BHkv = a.B * a.Hkv;
+  const long long grid = (long long)BHkv * n_kb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), CK::kLdsBytes, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, a.Hq, a.Hkv, a.Hq / a.Hkv, n_kb, a.scale, a.scale * kLog2e);
+                     a.N, BHkv, a.Hq, a.Hkv, a.Hq / a.Hkv, a.scale, a.scale * kLog2e,
+                     BHkv % 8 == 0 ? 1 : 0);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
-  using CQ = DqCfg<D, kNwQ>;
-  auto kern = bwd_dq_kernel<D, kNwQ, CAUSAL>;
+  using CQ = DqCfg<D, kDqBC, kDqNW>;
+  auto kern = bwd_dq_kernel<D, kDqBC, kDqNW, kDqWPE, CAUSAL>;
   static const hipError_t attr = allow_lds(kern, CQ::kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;

@@ -52,98 +52,9 @@ __device__ __forceinline__ float swap_halves(float x) {
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
-// Interleave 4 rows of 8 bf16 (one 16-byte value each) into 8 columns of
-// 4 bf16: out[j] = {r0[j], r1[j], r2[j], r3[j]} packed in 8 bytes.  Used to
-// store a K/V tile "4 keys per d" so that a transposed MFMA operand is two
-// 8-byte LDS reads.
-__device__ __forceinline__ void interleave4x8(const u32x4 (&r)[4], u32x2 (&out)[8]) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a = r[0][w], b = r[1][w], c = r[2][w], d = r[3][w];
-    // even column 2w: low halves; odd column 2w+1: high halves
-    out[2 * w][0] = (a & 0xFFFFu) | (b << 16);
-    out[2 * w][1] = (c & 0xFFFFu) | (d << 16);
-    out[2 * w + 1][0] = (a >> 16) | (b & 0xFFFF0000u);
-    out[2 * w + 1][1] = (c >> 16) | (d & 0xFFFF0000u);
-  }
-}
-
 }  // namespace attn
 
 namespace attn {
-
-// Stages an R x D bf16 tile (rows row0.., rows >= N read as zero) from global
-// memory through registers into LDS, in units of 4 rows x 8 columns per
-// thread.  store() can write two LDS copies from one load:
-//   row-major, rows `stride` bytes apart (16 bytes of padding per row keep
-//   16-byte reads of 32 consecutive rows free of bank conflicts), and
-//   "4 rows per column": for each group of 4 rows, D entries of 8 bytes
-//   holding rows 4g..4g+3 of one column, so a transposed MFMA operand is two
-//   8-byte reads.
-template <int D, int R, int NT>
-struct TileStager {
-  static constexpr int kUnits = (R / 4) * (D / 8);
-  static constexpr int kPer = (kUnits + NT - 1) / NT;
-  static constexpr int kRowStride = D * 2 + 16;   // bytes, row-major copy
-  static constexpr int kGroupBytes = D * 8;       // bytes, one 4-row group
-  static constexpr int kRowMajorBytes = R * kRowStride;
-  static constexpr int kInterleavedBytes = (R / 4) * kGroupBytes;
-  u32x4 reg[kPer][4];
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int row0, int N, int tid) {
-#pragma unroll
-    for (int it = 0; it < kPer; ++it) {
-      const int u = it * NT + tid;
-      if (kUnits % NT == 0 || u < kUnits) {
-        const int g = u / (D / 8), c = u % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = row0 + 4 * g + r;
-          reg[it][r] = row < N ? *(const u32x4*)(base + (size_t)row * D + c * 8) : zero4();
-        }
-      }
-    }
-  }
-
-  template <bool ROWMAJOR, bool INTERLEAVED>
-  __device__ __forceinline__ void store(unsigned char* rm, unsigned char* il, int tid) const {
-#pragma unroll
-    for (int it = 0; it < kPer; ++it) {
-      const int u = it * NT + tid;
-      if (kUnits % NT == 0 || u < kUnits) {
-        const int g = u / (D / 8), c = u % (D / 8);
-        if (ROWMAJOR) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) *(u32x4*)(rm + (4 * g + r) * kRowStride + c * 16) = reg[it][r];
-        }
-        if (INTERLEAVED) {
-          u32x2 t[8];
-          interleave4x8(reg[it], t);
-          unsigned char* dst = il + g * kGroupBytes + c * 64;
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *(u32x4*)(dst + 16 * j) = u32x4{t[2 * j][0], t[2 * j][1], t[2 * j + 1][0], t[2 * j + 1][1]};
-        }
-      }
-    }
-  }
-};
-
-// A operand (lane: row l%32, 8 consecutive columns) read from a row-major
-// LDS copy: rows row0 + l%32, columns 16*slab + 8*(l/32) .. +7.
-template <int STRIDE>
-__device__ __forceinline__ u32x4 lds_row_frag(const unsigned char* rm, int row0, int slab, int l32, int hi) {
-  return *(const u32x4*)(rm + (row0 + l32) * STRIDE + (slab * 16 + 8 * hi) * 2);
-}
-
-// Transposed A operand from a "4 rows per column" LDS copy: column `col`,
-// k slots 0..3 = rows 4*g0 .. 4*g0+3, k slots 4..7 = rows 4*(g0+2) .. +3.
-template <int GROUP_BYTES>
-__device__ __forceinline__ u32x4 lds_tr_frag(const unsigned char* il, int g0, int col) {
-  const u32x2 lo = *(const u32x2*)(il + g0 * GROUP_BYTES + col * 8);
-  const u32x2 up = *(const u32x2*)(il + (g0 + 2) * GROUP_BYTES + col * 8);
-  return u32x4{lo[0], lo[1], up[0], up[1]};
-}
 
 // Eight fp32 values -> one bf16x8 MFMA operand (round to nearest even).
 __device__ __forceinline__ u32x4 pack8(const float* p) {
@@ -153,5 +64,62 @@ __device__ __forceinline__ u32x4 pack8(const float* p) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
+
+}  // namespace attn
+
+#include "attn_layout.h"
+
+namespace attn {
+
+// Wait for every outstanding memory operation of this wave (global loads,
+// including the direct-to-LDS ones, and LDS reads).
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Direct 16-byte global -> LDS loads of a ROWS x D tile (swizzled layout of
+// attn_layout.h) starting at global row row0 of `g` ([N, D] rows).  One
+// instruction moves 1 KB; the NW waves of the workgroup split the tile's
+// segments.  Rows at or past N repeat row N-1 (finite data; every kernel
+// masks those rows or keys out).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void direct_tile_load(const uint16_t* __restrict__ g, int row0, int N,
+                                                 unsigned char* tile, int wave, int lane) {
+  constexpr int kSegs = ROWS * 2 * D / 1024;
+  static_assert(kSegs * 1024 == ROWS * 2 * D, "tile is a whole number of 1 KB segments");
+#pragma unroll
+  for (int k = 0; k < (kSegs + NW - 1) / NW; ++k) {
+    const int seg = k * NW + wave;
+    if (kSegs % NW == 0 || seg < kSegs) {
+      int r, c;
+      layout::direct_src<D>(seg * 1024 + lane * 16, r, c);
+      const int gr = min(row0 + r, N - 1);
+      const uint16_t* src = g + (size_t)gr * D + c * 8;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)(tile + seg * 1024),
+                                       16, 0, 0);
+    }
+  }
+}
+
+// Row fragment (A or B operand): lane l gets row row0 + l%32, columns
+// 16*slab + 8*(l/32) .. +7 of a swizzled tile.
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const unsigned char* tile, int lane, int row0, int slab) {
+  return *(const u32x4*)(tile + layout::row_frag_off<D>(lane, row0, slab));
+}
+
+// Transposed A operand from a swizzled tile (two ds_read_b64_tr_b16): lane l
+// gets column col0 + l%32; slots 0..3 = rows row0 + 4*(l/32) + 0..3, slots
+// 4..7 = rows row0 + 8 + 4*(l/32) + 0..3.  row0 is a multiple of 16, col0 of 32.
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const unsigned char* tile, int lane, int row0, int col0) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + layout::tr_frag_off<D>(lane, row0, col0, 0)));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + layout::tr_frag_off<D>(lane, row0, col0, 1)));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
 
 }  // namespace attn
