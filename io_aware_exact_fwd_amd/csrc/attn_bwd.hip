@@ -124,30 +124,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64
   const int per_head = n_qt - qt0;
   const int n_iter = per_head * G;
 
-  auto issue = [&](int it, int buf) {
-    const int hh = it / per_head, qt = qt0 + it % per_head;
+  // the query tile of iteration it is (head hk*G + it / per_head, tile
+  // qt0 + it % per_head); both are stepped incrementally instead of divided
+  auto issue = [&](int hh, int qt, int buf) {
     const size_t qh_off = ((size_t)b * Hq + hk * G + hh) * N * D;
     direct_tile_load<D, BQ, NW>(Q + qh_off, qt * BQ, N, qtile(buf), wave, lane);
     direct_tile_load<D, BQ, NW>(dO + qh_off, qt * BQ, N, qtile(buf) + C::kQTile, wave, lane);
   };
-  float stat_reg = 0.f;   // threads 0..63: LSE*log2(e) of a row; 64..127: its D
-  auto load_stats = [&](int it) {
-    if (tid < 2 * BQ) {
-      const int hh = it / per_head, qt = qt0 + it % per_head;
-      const int row = qt * BQ + (tid & (BQ - 1));
+  // Threads 0..63 fetch the LSE of one row of the tile, threads 64..127 its D.
+  // The raw value stays in a register until store_stats, after the tile's
+  // math, so the load's latency hides under that math; rows past N become
+  // LSE = +inf (P = 0) and D = 0.
+  float stat_raw = 0.f;
+  bool stat_valid = false;
+  auto load_stats = [&](int hh, int qt) {
+    const int row = qt * BQ + (tid & (BQ - 1));
+    stat_valid = tid < 2 * BQ && row < N;
+    if (stat_valid) {
       const size_t idx = ((size_t)b * Hq + hk * G + hh) * N + row;
-      if (tid < BQ) stat_reg = row < N ? LSE[idx] * kLog2e : INFINITY;   // rows >= N: P = 0
-      else stat_reg = row < N ? Dl[idx] : 0.f;
+      stat_raw = (tid < BQ ? LSE : Dl)[idx];
     }
   };
   auto store_stats = [&](int buf) {
-    if (tid < 2 * BQ) stats(buf)[tid] = stat_reg;
+    if (tid < BQ) stats(buf)[tid] = stat_valid ? stat_raw * kLog2e : INFINITY;
+    else if (tid < 2 * BQ) stats(buf)[tid] = stat_valid ? stat_raw : 0.f;
   };
 
   direct_tile_load<D, C::kBKV, NW>(K + kv_off, k0, N, Kt, wave, lane);
   direct_tile_load<D, C::kBKV, NW>(V + kv_off, k0, N, Vt, wave, lane);
-  issue(0, 0);
-  load_stats(0);
+  int hh_n = 0, qt_n = qt0;     // the tile most recently issued
+  issue(hh_n, qt_n, 0);
+  load_stats(hh_n, qt_n);
   store_stats(0);
   wait_all_memory();
   __syncthreads();
@@ -161,11 +168,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64
 
   for (int it = 0; it < n_iter; ++it) {
     const int buf = it & 1;
+    const int qs = qt_n * BQ + 32 * qh;   // first query row of this wave in tile it
     if (it + 1 < n_iter) {
-      issue(it + 1, buf ^ 1);
-      load_stats(it + 1);
+      if (++qt_n == n_qt) {
+        qt_n = qt0;
+        ++hh_n;
+      }
+      issue(hh_n, qt_n, buf ^ 1);
+      load_stats(hh_n, qt_n);
     }
-    const int qs = (qt0 + it % per_head) * BQ + 32 * qh;   // first query row of this wave
     if (kw0 < N && !(CAUSAL && qs + 31 < kw0)) {
       const unsigned char* Qt = qtile(buf);
       const unsigned char* dOt = Qt + C::kQTile;
@@ -395,8 +406,8 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
 
 // dK/dV: 4 key groups x 2 query halves = 8 waves, 128 keys per workgroup.
 constexpr int kDkdvNWK = 4, kDkdvWPE = 2;
-// dQ: 8 waves x 32 queries, 64-key tiles.
-constexpr int kDqBC = 64, kDqNW = 8, kDqWPE = 2;
+// dQ: 8 waves x 32 queries, 128-key tiles (128 KB of double-buffered LDS).
+constexpr int kDqBC = 128, kDqNW = 8, kDqWPE = 2;
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {

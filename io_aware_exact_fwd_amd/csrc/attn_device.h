@@ -44,10 +44,18 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value held by lane (l ^ 32): the partner that holds the other half of a
-// row in the 32x32 C layout.
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// max / sum of x over the lane pair (l, l^32) -- the two halves of a column
+// in the 32x32 C layout.  v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second; with x in both, one of the
+// two results holds the partner's value and the other x itself, so the
+// symmetric op of the two results is the pair's max / sum in every lane.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
@@ -74,6 +82,24 @@ namespace attn {
 // Wait for every outstanding memory operation of this wave (global loads,
 // including the direct-to-LDS ones, and LDS reads).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Workgroup barrier for tiles filled by direct loads.  Each wave first waits
+// until at most N of its vector-memory operations are outstanding (they
+// complete in issue order, so every direct load but the N most recent has
+// written LDS) and all its LDS operations are done; then s_barrier.  Unlike
+// __syncthreads() this does not wait for *every* outstanding load, so a
+// prefetch issued before the barrier stays in flight across it.  The empty
+// asm statements keep the compiler from moving memory accesses across.
+// s_waitcnt immediate on gfx9: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits
+// 15:14, expcnt in bits 6:4 (7 = no wait), lgkmcnt in bits 11:8.
+template <int N>
+__device__ __forceinline__ void barrier_vmem_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Direct 16-byte global -> LDS loads of a ROWS x D tile (swizzled layout of
 // attn_layout.h) starting at global row row0 of `g` ([N, D] rows).  One
