@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "bwd_pre_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
     "bwd_dkdv_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
     "bwd_dq_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
+    "bwd_grads_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -222,9 +223,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     # Each phase is one kernel launch; events between them give per-kernel
-    # durations on the stream the kernels run on.  The three backward phases
-    # are exactly what attn_bwd runs, in the same order.
-    phases = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if w.with_grad else [])
+    # durations on the stream the kernels run on.  The two backward phases are
+    # exactly what attn_bwd runs, in the same order.
+    phases = ["fwd"] + (["bwd_pre", "bwd_grads"] if w.with_grad else [])
 
     def step(ev=None):
         def mark(i):
@@ -236,10 +237,9 @@ def main():
         if w.with_grad:
             attn.bwd_preprocess(o, do, delta, stream=stream)
             mark(2)
-            attn.bwd_dkdv(q, k, v, do, lse, delta, causal=True, dk=dk, dv=dv, stream=stream)
+            attn.bwd_grads(q, k, v, do, lse, delta, causal=True, dq=dq, dk=dk, dv=dv,
+                           stream=stream)
             mark(3)
-            attn.bwd_dq(q, k, v, do, lse, delta, causal=True, dq=dq, stream=stream)
-            mark(4)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -265,11 +265,12 @@ def main():
     ms_per_step = wall * 1e3 / steps
     pairs = w.pairs(True)
     # algorithmic matmul FLOPs per unmasked pair, by kernel: the forward's QK^T
-    # and PV (4d); the dK/dV kernel's S, dP, dV and dK (8d); the dQ kernel's dQ
-    # (2d -- its S and dP are recomputation); the pre-pass does no matmul.
-    per_pair = {"fwd": 4 * w.d, "bwd_pre": 0, "bwd_dkdv": 8 * w.d, "bwd_dq": 2 * w.d}
+    # and PV (4d); the gradient kernel's S, dP, dV, dK and dQ (10d -- the dQ
+    # blocks' second S and dP are recomputation and not counted); the pre-pass
+    # does no matmul.
+    per_pair = {"fwd": 4 * w.d, "bwd_pre": 0, "bwd_grads": 10 * w.d}
     kernel_name = {"fwd": "attn_fwd_kernel", "bwd_pre": "bwd_pre_kernel",
-                   "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
+                   "bwd_grads": "bwd_grads_kernel"}
     fwd_flops = w.fwd_flops(True)
     bwd_flops = w.bwd_flops(True) if w.with_grad else 0
     step_flops = fwd_flops + bwd_flops

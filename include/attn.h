@@ -113,9 +113,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              void* stream);
 
 /*
- * The three stages attn_bwd runs, in this order, for callers that schedule
- * them themselves -- for instance dK/dV and dQ on two streams, since both read
- * only the inputs, the LSE and delta.  Same conventions and errors as attn_bwd.
+ * The stages of attn_bwd, for callers that schedule them themselves.  attn_bwd
+ * is attn_bwd_preprocess followed by attn_bwd_grads; attn_bwd_grads computes
+ * bitwise what attn_bwd_dkdv and attn_bwd_dq compute, in one launch.  The
+ * gradient stages read only the inputs, the LSE and delta, so they may run on
+ * different streams once delta is written.  Same conventions and errors as
+ * attn_bwd.
  *
  * attn_bwd_preprocess: delta [B, Hq, N] fp32 (caller-owned, e.g. the first
  *   B*Hq*N*4 bytes of attn_bwd's workspace) = rowsum(dO * O), which equals the
@@ -123,6 +126,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
  * attn_bwd_dkdv: dK, dV [B, Hkv, N, d] bf16, each summed over the Hq/Hkv query
  *   heads of its group, recomputing probabilities from lse ([LONGCTX] §2.2).
  * attn_bwd_dq: dQ [B, Hq, N, d] bf16, recomputing probabilities from lse.
+ * attn_bwd_grads: dQ, dK and dV as the two calls above give them.
  */
 int attn_bwd_preprocess(const void* o, const void* dout, float* delta,
                         int B, int Hq, int N, int d, void* stream);
@@ -134,6 +138,10 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                 const float* lse, const float* delta, void* dq,
                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                 void* stream);
+int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dout,
+                   const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   void* stream);
 
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
  * of the last failure on the calling thread.  Never NULL. */

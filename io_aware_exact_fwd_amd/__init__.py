@@ -19,13 +19,15 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime that libattn.so then binds to
 
 __all__ = [
-    "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
+    "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads",
+    "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
-            "attn_bwd_dkdv", "attn_bwd_dq", "attn_strerror", "attn_device_check")
+            "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads", "attn_strerror",
+            "attn_device_check")
 
 ATTN_OK = 0
 
@@ -59,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dkdv.restype = i
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.attn_bwd_dq.restype = i
+    L.attn_bwd_grads.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_bwd_grads.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_strerror.argtypes = [i]
@@ -216,3 +220,24 @@ def bwd_dq(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[float] 
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_bwd_dq")
     return dq
+
+
+def bwd_grads(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[float] = None,
+              dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+              dv: Optional[torch.Tensor] = None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV (bf16) in one launch: what bwd_dkdv and bwd_dq give, bitwise."""
+    B, Hq, Hkv, N, d = _stage_checks(q, k, v, do, lse, delta)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_bf16("dq", dq, (B, Hq, N, d))
+    _check_bf16("dk", dk, (B, Hkv, N, d))
+    _check_bf16("dv", dv, (B, Hkv, N, d))
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_bwd_grads(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                              _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
+                              int(bool(causal)), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_grads")
+    return dq, dk, dv

@@ -132,14 +132,14 @@ ATTN_EXPORT int attn_bwd_preprocess(const void* o, const void* dout, float* delt
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_preprocess launch");
 }
 
-// Shared checks of the two recomputing stages.
+// Shared checks of the recomputing stages (out1..out3 are their outputs).
 static int check_stage(const void* q, const void* k, const void* v, const void* dout,
                        const float* lse, const float* delta, const void* out1, const void* out2,
-                       int B, int Hq, int Hkv, int N, int d, float scale) {
-  if (!q || !k || !v || !dout || !lse || !delta || !out1 || !out2) return ATTN_ERR_NULL;
+                       const void* out3, int B, int Hq, int Hkv, int N, int d, float scale) {
+  if (!q || !k || !v || !dout || !lse || !delta || !out1 || !out2 || !out3) return ATTN_ERR_NULL;
   int rc = check_problem(B, Hq, Hkv, N, d);
   if (rc) return rc;
-  const void* ptrs[] = {q, k, v, dout, lse, delta, out1, out2};
+  const void* ptrs[] = {q, k, v, dout, lse, delta, out1, out2, out3};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
   if ((rc = check_scale(scale))) return rc;
@@ -150,7 +150,7 @@ ATTN_EXPORT int attn_bwd_dkdv(const void* q, const void* k, const void* v, const
                               const float* lse, const float* delta, void* dk, void* dv, int B,
                               int Hq, int Hkv, int N, int d, int causal, float scale,
                               void* stream) {
-  int rc = check_stage(q, k, v, dout, lse, delta, dk, dv, B, Hq, Hkv, N, d, scale);
+  int rc = check_stage(q, k, v, dout, lse, delta, dk, dv, dv, B, Hq, Hkv, N, d, scale);
   if (rc) return rc;
   attn::BwdArgs a{q, k, v, nullptr, lse, dout, nullptr, dk, dv, (float*)delta,
                   B, Hq, Hkv, N, d, causal != 0, scale};
@@ -161,12 +161,24 @@ ATTN_EXPORT int attn_bwd_dkdv(const void* q, const void* k, const void* v, const
 ATTN_EXPORT int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                             const float* lse, const float* delta, void* dq, int B, int Hq,
                             int Hkv, int N, int d, int causal, float scale, void* stream) {
-  int rc = check_stage(q, k, v, dout, lse, delta, dq, dq, B, Hq, Hkv, N, d, scale);
+  int rc = check_stage(q, k, v, dout, lse, delta, dq, dq, dq, B, Hq, Hkv, N, d, scale);
   if (rc) return rc;
   attn::BwdArgs a{q, k, v, nullptr, lse, dout, dq, nullptr, nullptr, (float*)delta,
                   B, Hq, Hkv, N, d, causal != 0, scale};
   hipError_t e = attn::launch_bwd_dq(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_dq launch");
+}
+
+ATTN_EXPORT int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const float* delta, void* dq, void* dk,
+                               void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
+                               float scale, void* stream) {
+  int rc = check_stage(q, k, v, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, d, scale);
+  if (rc) return rc;
+  attn::BwdArgs a{q, k, v, nullptr, lse, dout, dq, dk, dv, (float*)delta,
+                  B, Hq, Hkv, N, d, causal != 0, scale};
+  hipError_t e = attn::launch_bwd_grads(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_grads launch");
 }
 
 ATTN_EXPORT const char* attn_strerror(int code) {

@@ -77,20 +77,19 @@ struct DkdvCfg {
   static_assert(kRedBytes <= kLdsBytes, "reduction fits in the tile memory");
 };
 
-template <int D, int NWK, int WPE, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64),
-                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_dkdv_kernel(
+// One dK/dV workgroup: w is its index in the dK/dV grid, smem its LDS.
+template <int D, int NWK, bool CAUSAL>
+__device__ __forceinline__ void dkdv_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
-    float scale, float scale_log2, int xcd_remap) {
+    float scale, float scale_log2, int xcd_remap, int w, unsigned char* smem) {
   using C = DkdvCfg<D, NWK>;
   constexpr int NW = C::kNW;
   constexpr int BQ = C::kBQ;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
 
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int kg = wave % NWK;      // key group: keys kw0 .. kw0+31
   const int qh = wave / NWK;      // query half: rows 32*qh .. 32*qh+31 of each tile
@@ -99,7 +98,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64
   // B*Hkv is a multiple of 8 all key blocks of one K/V head share an XCD, so
   // the Q/dO tiles they all read stay in that XCD's L2
   int bhk, kb;
-  const int w = blockIdx.x;
   if (xcd_remap) {
     const int hx = BHkv >> 3;
     const int i = w >> 3;
@@ -266,6 +264,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64
   }
 }
 
+template <int D, int NWK, int WPE, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64),
+                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
+    float scale, float scale_log2, int xcd_remap) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  dkdv_block<D, NWK, CAUSAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale, scale_log2,
+                             xcd_remap, blockIdx.x, smem);
+}
+
 // ---------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------
@@ -277,23 +287,21 @@ struct DqCfg {
   static constexpr int kLdsBytes = 2 * 2 * kTile;   // double-buffered K and V
 };
 
-template <int D, int BC, int NW, int WPE, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
-                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_dq_kernel(
+// One dQ workgroup: w is its index in the dQ grid, smem its LDS.
+template <int D, int BC, int NW, bool CAUSAL>
+__device__ __forceinline__ void dq_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
-    float scale_log2, int xcd_remap) {
+    float scale_log2, int xcd_remap, int w, unsigned char* smem) {
   using C = DqCfg<D, BC, NW>;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KB = BC / 32;
 
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
   int bh, qrank;
-  const int w = blockIdx.x;
   if (xcd_remap) {
     const int hx = BH >> 3;
     const int i = w >> 3;
@@ -390,6 +398,41 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   }
 }
 
+template <int D, int BC, int NW, int WPE, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
+    float scale_log2, int xcd_remap) {
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  dq_block<D, BC, NW, CAUSAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale, scale_log2,
+                              xcd_remap, blockIdx.x, smem);
+}
+
+// dK/dV and dQ in one launch: workgroups [0, n_dkdv) are dK/dV blocks and the
+// rest dQ blocks.  The two halves are independent (both read only the inputs,
+// LSE and D), so dQ blocks fill the CUs that dK/dV blocks release instead of
+// waiting for the whole dK/dV grid to drain.  Both halves use 8 waves.
+template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
+                          amdgpu_waves_per_eu(WPE, WPE))) void bwd_grads_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
+    uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
+    int BHkv, int BH, int Hq, int Hkv, int G, int n_dkdv, int n_qb, float scale, float scale_log2,
+    int xcd_kv, int xcd_q) {
+  static_assert(2 * NWK == NW, "both halves run the same number of waves");
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  const int w = blockIdx.x;
+  if (w < n_dkdv)
+    dkdv_block<D, NWK, CAUSAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale, scale_log2,
+                               xcd_kv, w, smem);
+  else
+    dq_block<D, BC, NW, CAUSAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
+                                scale_log2, xcd_q, w - n_dkdv, smem);
+}
+
 template <typename KernelT>
 hipError_t allow_lds(KernelT kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -444,7 +487,36 @@ hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_grads_t(const BwdArgs& a, hipStream_t stream) {
+  using CK = DkdvCfg<D, kDkdvNWK>;
+  using CQ = DqCfg<D, kDqBC, kDqNW>;
+  static_assert(CK::kThreads == CQ::kThreads, "one workgroup size for both halves");
+  constexpr int lds = CK::kLdsBytes > CQ::kLdsBytes ? CK::kLdsBytes : CQ::kLdsBytes;
+  auto kern = bwd_grads_kernel<D, kDkdvNWK, kDqBC, kDqNW, kDqWPE, CAUSAL>;
+  static const hipError_t attr = allow_lds(kern, lds);
+  if (attr != hipSuccess) return attr;
+  const int BHkv = a.B * a.Hkv, BH = a.B * a.Hq;
+  const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
+  const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
+  const long long n_dkdv = (long long)BHkv * n_kb;
+  const long long grid = n_dkdv + (long long)BH * n_qb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), lds, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,
+                     (uint16_t*)a.dv, a.N, BHkv, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, (int)n_dkdv, n_qb,
+                     a.scale, a.scale * kLog2e, BHkv % 8 == 0 ? 1 : 0, BH % 8 == 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream) {
+  if (a.d == 128)
+    return a.causal ? launch_grads_t<128, true>(a, stream) : launch_grads_t<128, false>(a, stream);
+  return a.causal ? launch_grads_t<64, true>(a, stream) : launch_grads_t<64, false>(a, stream);
+}
 
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
   return a.d == 128 ? launch_pre_t<128>(a, stream) : launch_pre_t<64>(a, stream);
@@ -464,9 +536,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = launch_bwd_pre(a, stream);
-  if (e == hipSuccess) e = launch_bwd_dkdv(a, stream);
-  if (e == hipSuccess) e = launch_bwd_dq(a, stream);
-  return e;
+  return e == hipSuccess ? launch_bwd_grads(a, stream) : e;
 }
 
 }  // namespace attn

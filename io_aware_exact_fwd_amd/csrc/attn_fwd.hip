@@ -20,12 +20,8 @@
 //   * K and V tiles are copied global -> LDS by 16-byte direct loads (no
 //     staging registers) into row-major, XOR-swizzled tiles: K is read as
 //     row fragments, V^T with the transposing LDS read, both free of bank
-//     conflicts.  K and V are double-buffered in two separate LDS objects;
-//     the loads of K(j+1) start before tile j's scores and those of V(j+1)
-//     right after tile j's last V read, so neither ever waits for the other
-//     (the compiler would otherwise hold each transposing read until every
-//     direct load in flight had landed); two barriers per tile publish the
-//     K and the V halves;
+//     conflicts; tiles are double-buffered, the next tile's loads are in
+//     flight while the current one is computed, one barrier per tile;
 //   * two waves per SIMD, so one wave's softmax VALU work runs under the
 //     other's MFMAs;
 //   * causal: key tiles past a workgroup's last row are never loaded, a wave
@@ -47,9 +43,7 @@ struct FwdCfg {
   static constexpr int kThreads = NW * 64;
   static constexpr int kBR = NW * 32;               // query rows per workgroup
   static constexpr int kTile = BC * 2 * D;          // bytes of one K or V tile
-  static constexpr int kSegs = kTile / 1024;        // 1 KB direct-load segments per tile
-  static constexpr int kOps = kSegs / NW;           // direct loads per wave per tile
-  static_assert(kSegs % NW == 0, "every wave issues the same number of direct loads");
+  static constexpr int kLdsBytes = 2 * 2 * kTile;   // double-buffered K and V
   static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
 };
 
@@ -72,8 +66,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   constexpr int KB = BC / 32;  // 32-key blocks per tile
   constexpr int DB = D / 32;   // 32-wide d blocks of O^T
 
-  __shared__ __attribute__((aligned(1024))) unsigned char k_lds[2 * C::kTile];
-  __shared__ __attribute__((aligned(1024))) unsigned char v_lds[2 * C::kTile];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,11 +111,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const int kv_end = CAUSAL ? min(N, q0 + C::kBR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
-  auto issue_k = [&](int j, int buf) {
-    direct_tile_load<D, BC, NW>(Kp, j * BC, N, k_lds + buf * C::kTile, wave, lane);
-  };
-  auto issue_v = [&](int j, int buf) {
-    direct_tile_load<D, BC, NW>(Vp, j * BC, N, v_lds + buf * C::kTile, wave, lane);
+  auto issue_tile = [&](int j, int buf) {
+    unsigned char* kt = smem + buf * 2 * C::kTile;
+    direct_tile_load<D, BC, NW>(Kp, j * BC, N, kt, wave, lane);
+    direct_tile_load<D, BC, NW>(Vp, j * BC, N, kt + C::kTile, wave, lane);
   };
 
   // ---- running statistics and the O^T accumulator ----
@@ -131,22 +123,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  issue_k(0, 0);
-  issue_v(0, 0);
+  issue_tile(0, 0);
   wait_all_memory();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int kstart = j * BC;
-    const bool more = j + 1 < n_tiles;
-    if (more) issue_k(j + 1, buf ^ 1);
-    const bool active = wave_live && (!CAUSAL || kstart <= qw1);
-    const unsigned char* kt = k_lds + buf * C::kTile;
-    const unsigned char* vt = v_lds + buf * C::kTile;
-    u32x4 pf[KB][2];
+    if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
 
-    if (active) {
+    if (wave_live && (!CAUSAL || kstart <= qw1)) {
+      const unsigned char* kt = smem + buf * 2 * C::kTile;
+      const unsigned char* vt = kt + C::kTile;
 
       // S^T[x] = K_tile Q^T  (32 keys x 32 queries per accumulator)
       f32x16 s[KB];
@@ -187,6 +175,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       }
       // m_run is finite from the first visited tile on: key 0 is visible to every row
+      u32x4 pf[KB][2];
       float lsum = 0.f;
 #pragma unroll
       for (int x = 0; x < KB; ++x) {
@@ -200,13 +189,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         pf[x][1] = pack8(p + 8);
       }
       l_run += lsum;
-    }
 
-    // V(j) has landed everywhere (only K(j+1) may still be in flight)
-    if (more) barrier_vmem_at_most<C::kOps>();
-    else barrier_vmem_at_most<0>();
-
-    if (active) {
       // O^T[db] += V^T P^T: slab h2 of key block x holds keys
       // x*32 + 16*h2 + {4*hi..4*hi+3, 8+4*hi..8+4*hi+3} in this lane's k slots
 #pragma unroll
@@ -218,13 +201,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
             acc[db] = mfma_32x32x16(tr_frag<D>(vt, lane, x * 32 + 16 * h2, db * 32), pf[x][h2], acc[db]);
     }
 
-    // V(j+1) streams in during the next tile's scores; K(j+1) must be complete
-    if (more) {
-      issue_v(j + 1, buf ^ 1);
-      barrier_vmem_at_most<C::kOps>();
-    } else {
-      barrier_vmem_at_most<0>();
-    }
+    wait_all_memory();
+    __syncthreads();
   }
 
   if (!wave_live) return;
@@ -255,8 +233,12 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)BH * n_qb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto kern = attn_fwd_kernel<D, BC, NW, WPE, CAUSAL, LAG>;
+  // more than 64 KB of dynamic LDS has to be allowed once per kernel instance
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  if (attr != hipSuccess) return attr;
   const int xcd_remap = (BH % 8 == 0) ? 1 : 0;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), 0, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, n_qb,
                      a.scale * kLog2e, xcd_remap);

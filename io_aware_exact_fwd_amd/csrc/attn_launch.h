@@ -39,11 +39,13 @@ inline size_t bwd_workspace_bytes(int B, int Hq, int N) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-// The backward's stages; launch_bwd runs all three in order.  Each reads the
-// BwdArgs fields it needs (delta must be set for all of them).
+// The backward's stages.  Each reads the BwdArgs fields it needs (delta must
+// be set for all of them).  launch_bwd_grads runs dK/dV and dQ in one launch;
+// launch_bwd is launch_bwd_pre followed by launch_bwd_grads.
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
                                            "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
-                                           "attn_strerror", "attn_device_check"])
+                                           "attn_bwd_grads", "attn_strerror",
+                                           "attn_device_check"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -120,6 +121,12 @@ def test_stage_argument_errors(L):
     assert L.attn_bwd_dq(*args[:7], 1, 4, 2, 16, 128, 1, float("inf"), None) == 5
     assert L.attn_bwd_dq(*args[:6], MIS, 1, 4, 2, 16, 128, 1, 0.1, None) == 3
     assert L.attn_bwd_dq(A, A, A, A, None, A, A, 1, 4, 2, 16, 128, 1, 0.1, None) == 1
+    args = [A] * 9
+    assert L.attn_bwd_grads(*args, 1, 4, 3, 16, 128, 1, 0.1, None) == 2
+    assert L.attn_bwd_grads(*args[:8], None, 1, 4, 2, 16, 128, 1, 0.1, None) == 1
+    assert L.attn_bwd_grads(*args[:7], MIS, A, 1, 4, 2, 16, 128, 1, 0.1, None) == 3
+    assert L.attn_bwd_grads(*args, 1, 4, 2, 16, 100, 1, 0.1, None) == 3
+    assert L.attn_bwd_grads(*args, 1, 4, 2, 16, 128, 1, 0.0, None) == 5
 
 
 def test_strerror(L):

@@ -136,7 +136,7 @@ def test_bwd_workspace_errors(gpu_lib):
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_bwd_stages_equal_bwd(gpu_lib, causal):
-    """preprocess -> dkdv -> dq, called separately, give bitwise what attn_bwd gives."""
+    """preprocess -> dkdv -> dq and preprocess -> grads give bitwise what attn_bwd gives."""
     say(f"bwd stages causal={causal}")
     x = make_custom_inputs(2, 6, 2, 700, 128, seed=16, with_grad=True)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
@@ -145,8 +145,10 @@ def test_bwd_stages_equal_bwd(gpu_lib, causal):
     delta = gpu_lib.bwd_preprocess(o, do)
     dk2, dv2 = gpu_lib.bwd_dkdv(q, k, v, do, lse, delta, causal=causal)
     dq2 = gpu_lib.bwd_dq(q, k, v, do, lse, delta, causal=causal)
+    dq3, dk3, dv3 = gpu_lib.bwd_grads(q, k, v, do, lse, delta, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
     # delta is the softmax-Jacobian row term: rowsum(dO * O) of the bf16 tensors
     ref = (do.float() * o.float()).sum(-1)
     assert float((delta - ref).abs().max()) <= 1e-4 * float(ref.abs().max())
