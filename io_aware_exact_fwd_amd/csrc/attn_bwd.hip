@@ -124,10 +124,12 @@ __device__ __forceinline__ void dkdv_block(
 
   // the query tile of iteration it is (head hk*G + it / per_head, tile
   // qt0 + it % per_head); both are stepped incrementally instead of divided
+  TileLoader<D, BQ, NW> ldq;
+  ldq.init(wave, lane);
   auto issue = [&](int hh, int qt, int buf) {
     const size_t qh_off = ((size_t)b * Hq + hk * G + hh) * N * D;
-    direct_tile_load<D, BQ, NW>(Q + qh_off, qt * BQ, N, qtile(buf), wave, lane);
-    direct_tile_load<D, BQ, NW>(dO + qh_off, qt * BQ, N, qtile(buf) + C::kQTile, wave, lane);
+    ldq.load(Q + qh_off, qt * BQ, N, qtile(buf), wave);
+    ldq.load(dO + qh_off, qt * BQ, N, qtile(buf) + C::kQTile, wave);
   };
   // Threads 0..63 fetch the LSE of one row of the tile, threads 64..127 its D.
   // The raw value stays in a register until store_stats, after the tile's
@@ -148,8 +150,12 @@ __device__ __forceinline__ void dkdv_block(
     else if (tid < 2 * BQ) stats(buf)[tid] = stat_valid ? stat_raw : 0.f;
   };
 
-  direct_tile_load<D, C::kBKV, NW>(K + kv_off, k0, N, Kt, wave, lane);
-  direct_tile_load<D, C::kBKV, NW>(V + kv_off, k0, N, Vt, wave, lane);
+  {
+    TileLoader<D, C::kBKV, NW> ldk;
+    ldk.init(wave, lane);
+    ldk.load(K + kv_off, k0, N, Kt, wave);
+    ldk.load(V + kv_off, k0, N, Vt, wave);
+  }
   int hh_n = 0, qt_n = qt0;     // the tile most recently issued
   issue(hh_n, qt_n, 0);
   load_stats(hh_n, qt_n);
@@ -335,10 +341,12 @@ __device__ __forceinline__ void dq_block(
 
   const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
+  TileLoader<D, BC, NW> ldk;
+  ldk.init(wave, lane);
   auto issue_tile = [&](int j, int buf) {
     unsigned char* kt = smem + buf * 2 * C::kTile;
-    direct_tile_load<D, BC, NW>(K + kv_off, j * BC, N, kt, wave, lane);
-    direct_tile_load<D, BC, NW>(V + kv_off, j * BC, N, kt + C::kTile, wave, lane);
+    ldk.load(K + kv_off, j * BC, N, kt, wave);
+    ldk.load(V + kv_off, j * BC, N, kt + C::kTile, wave);
   };
   issue_tile(0, 0);
   wait_all_memory();

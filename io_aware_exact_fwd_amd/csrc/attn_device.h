@@ -79,6 +79,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 namespace attn {
 
+// Instruction classes for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
 // Wait for every outstanding memory operation of this wave (global loads,
 // including the direct-to-LDS ones, and LDS reads).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
@@ -102,29 +106,58 @@ __device__ __forceinline__ void barrier_vmem_at_most() {
 }
 
 // Direct 16-byte global -> LDS loads of a ROWS x D tile (swizzled layout of
-// attn_layout.h) starting at global row row0 of `g` ([N, D] rows).  One
-// instruction moves 1 KB; the NW waves of the workgroup split the tile's
-// segments.  Rows at or past N repeat row N-1 (finite data; every kernel
-// masks those rows or keys out).
+// attn_layout.h): one global_load_lds_dwordx4 moves 1 KB (lane i's 16 bytes
+// land at LDS base + 16 i), and the NW waves of the workgroup split the tile's
+// segments.  Rows at or past N repeat row N-1 (finite data; every kernel masks
+// those rows or keys out).
+//
+// The loads are issued from inline asm with a wave-uniform SGPR base and a
+// 32-bit VGPR byte offset.  Two reasons: the per-lane part of each segment's
+// offset is a single loop-invariant VGPR (not a 64-bit address per segment),
+// and the compiler's wait-count pass does not see an LDS DMA in flight --
+// when it does, it drains every outstanding LDS read (lgkmcnt(0)) before each
+// MFMA that consumes one, which serialises the LDS latency.  The asm has no
+// register outputs (the data goes to LDS), so nothing in flight can land in a
+// reused register; the one consequence is that the compiler never waits for
+// these loads, so every kernel waits for them itself (wait_all_memory() or
+// barrier_vmem_at_most<N>()) before the barrier that publishes the tile.
+// Byte offsets stay below 2^32 because N * D < 2^31 is checked on the host.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void direct_tile_load(const uint16_t* __restrict__ g, int row0, int N,
-                                                 unsigned char* tile, int wave, int lane) {
-  constexpr int kSegs = ROWS * 2 * D / 1024;
+struct TileLoader {
+  static constexpr int kSegs = ROWS * 2 * D / 1024;
+  static constexpr int kPer = (kSegs + NW - 1) / NW;   // segments per wave
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowShift = D == 128 ? 8 : 7;
   static_assert(kSegs * 1024 == ROWS * 2 * D, "tile is a whole number of 1 KB segments");
+  static_assert((1 << kRowShift) == kRowBytes, "row size");
+  unsigned rc[kPer];   // this lane's (row << kRowShift) | (chunk * 16) in each segment
+
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-  for (int k = 0; k < (kSegs + NW - 1) / NW; ++k) {
-    const int seg = k * NW + wave;
-    if (kSegs % NW == 0 || seg < kSegs) {
+    for (int k = 0; k < kPer; ++k) {
       int r, c;
-      layout::direct_src<D>(seg * 1024 + lane * 16, r, c);
-      const int gr = min(row0 + r, N - 1);
-      const uint16_t* src = g + (size_t)gr * D + c * 8;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)(tile + seg * 1024),
-                                       16, 0, 0);
+      layout::direct_src<D>((k * NW + wave) * 1024 + lane * 16, r, c);
+      rc[k] = ((unsigned)r << kRowShift) | (unsigned)(c * 16);
     }
   }
-}
+  // Rows row0 .. row0+ROWS-1 of the [N, D] matrix at g into `tile`.
+  __device__ __forceinline__ void load(const uint16_t* g, int row0, int N, unsigned char* tile,
+                                       int wave) const {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int seg = k * NW + wave;
+      if (kSegs % NW == 0 || seg < kSegs) {
+        const unsigned row = min((unsigned)row0 + (rc[k] >> kRowShift), (unsigned)(N - 1));
+        const unsigned voff = (row << kRowShift) | (rc[k] & (kRowBytes - 1));
+        const unsigned lds = (unsigned)(uintptr_t)(tile + seg * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(g)
+                     : "memory", "m0");
+      }
+    }
+  }
+};
 
 // Row fragment (A or B operand): lane l gets row row0 + l%32, columns
 // 16*slab + 8*(l/32) .. +7 of a swizzled tile.

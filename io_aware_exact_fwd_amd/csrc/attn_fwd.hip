@@ -62,6 +62,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
     int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale_log2, int xcd_remap) {
   using C = FwdCfg<D, BC, NW>;
+  constexpr int kPrefetch = 6; // K fragments in flight ahead of their MFMA
   constexpr int DS = D / 16;   // k-slabs of the QK^T contraction
   constexpr int KB = BC / 32;  // 32-key blocks per tile
   constexpr int DB = D / 32;   // 32-wide d blocks of O^T
@@ -111,10 +112,12 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const int kv_end = CAUSAL ? min(N, q0 + C::kBR) : N;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
+  TileLoader<D, BC, NW> ldr;
+  ldr.init(wave, lane);
   auto issue_tile = [&](int j, int buf) {
     unsigned char* kt = smem + buf * 2 * C::kTile;
-    direct_tile_load<D, BC, NW>(Kp, j * BC, N, kt, wave, lane);
-    direct_tile_load<D, BC, NW>(Vp, j * BC, N, kt + C::kTile, wave, lane);
+    ldr.load(Kp, j * BC, N, kt, wave);
+    ldr.load(Vp, j * BC, N, kt + C::kTile, wave);
   };
 
   // ---- running statistics and the O^T accumulator ----
@@ -136,14 +139,33 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       const unsigned char* kt = smem + buf * 2 * C::kTile;
       const unsigned char* vt = kt + C::kTile;
 
-      // S^T[x] = K_tile Q^T  (32 keys x 32 queries per accumulator)
+      // S^T[x] = K_tile Q^T  (32 keys x 32 queries per accumulator).  The K
+      // fragments go through a ring of kPrefetch registers, each read issued
+      // kPrefetch MFMAs before its use, and the scheduling groups keep the
+      // compiler to one read per MFMA so the LDS latency hides under them.
       f32x16 s[KB];
 #pragma unroll
       for (int x = 0; x < KB; ++x) s[x] = f32x16{};
+      {
+        constexpr int NSI = DS * KB;   // step i: key block i % KB, slab i / KB
+        u32x4 kr[kPrefetch];
 #pragma unroll
-      for (int sl = 0; sl < DS; ++sl)
+        for (int i = 0; i < kPrefetch; ++i) kr[i] = row_frag<D>(kt, lane, (i % KB) * 32, i / KB);
 #pragma unroll
-        for (int x = 0; x < KB; ++x) s[x] = mfma_32x32x16(row_frag<D>(kt, lane, x * 32, sl), qf[sl], s[x]);
+        for (int i = 0; i < NSI; ++i) {
+          const u32x4 a = kr[i % kPrefetch];
+          const int n = i + kPrefetch;
+          if (n < NSI) kr[i % kPrefetch] = row_frag<D>(kt, lane, (n % KB) * 32, n / KB);
+          s[i % KB] = mfma_32x32x16(a, qf[i / KB], s[i % KB]);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+        for (int i = 0; i < NSI - kPrefetch; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
+      }
 
       // mask: only tiles that cross the diagonal or the ragged end
       const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0);
