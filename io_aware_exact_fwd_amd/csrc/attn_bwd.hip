@@ -85,6 +85,7 @@ __device__ __forceinline__ void dkdv_block(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
     float scale, float scale_log2, int xcd_remap, int w, unsigned char* smem) {
   using C = DkdvCfg<D, NWK>;
+  constexpr int kPrefetch = 3;   // (A, B) fragment pairs in flight ahead of their MFMA
   constexpr int NW = C::kNW;
   constexpr int BQ = C::kBQ;
   constexpr int DS = D / 16;
@@ -188,11 +189,36 @@ __device__ __forceinline__ void dkdv_block(
       const float* del_l = lse_l + BQ;
 
       // S = Q K^T and dP = dO V^T: 32 queries x 32 keys, lane holds key column l%32
+      // Step i uses slab i/2 of (Q, K) for S (even i) or of (dO, V) for dP
+      // (odd i); both operands go through a ring of kPrefetch register pairs.
       f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        constexpr int NSI = 2 * DS;
+        auto fa = [&](int i) { return row_frag<D>((i & 1) ? dOt : Qt, lane, 32 * qh, i >> 1); };
+        auto fb = [&](int i) { return row_frag<D>((i & 1) ? Vt : Kt, lane, 32 * kg, i >> 1); };
+        u32x4 ra[kPrefetch], rb[kPrefetch];
 #pragma unroll
-      for (int sl = 0; sl < DS; ++sl) {
-        s = mfma_32x32x16(row_frag<D>(Qt, lane, 32 * qh, sl), row_frag<D>(Kt, lane, 32 * kg, sl), s);
-        dp = mfma_32x32x16(row_frag<D>(dOt, lane, 32 * qh, sl), row_frag<D>(Vt, lane, 32 * kg, sl), dp);
+        for (int i = 0; i < kPrefetch; ++i) {
+          ra[i] = fa(i);
+          rb[i] = fb(i);
+        }
+#pragma unroll
+        for (int i = 0; i < NSI; ++i) {
+          const u32x4 a = ra[i % kPrefetch], bb = rb[i % kPrefetch];
+          if (i + kPrefetch < NSI) {
+            ra[i % kPrefetch] = fa(i + kPrefetch);
+            rb[i % kPrefetch] = fb(i + kPrefetch);
+          }
+          if (i & 1) dp = mfma_32x32x16(a, bb, dp);
+          else s = mfma_32x32x16(a, bb, s);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefetch, 0);
+#pragma unroll
+        for (int i = 0; i < NSI - kPrefetch; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
       }
 
       // P = 2^(s*tau*log2e - LSE*log2e), dS = P (dP - D); rows 8r + 4hi + 0..3
@@ -301,6 +327,7 @@ __device__ __forceinline__ void dq_block(
     uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
     float scale_log2, int xcd_remap, int w, unsigned char* smem) {
   using C = DqCfg<D, BC, NW>;
+  constexpr int kPrefetch = 6;   // K/V fragments in flight ahead of their MFMA
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
   constexpr int KB = BC / 32;
@@ -363,11 +390,29 @@ __device__ __forceinline__ void dq_block(
 #pragma unroll
       for (int x = 0; x < KB; ++x) {
         // S^T and dP^T: 32 keys x 32 queries, lane holds query column l%32
+        // Step i reads slab i/2 of K (even i) or V (odd i); the fragments go
+        // through a ring of kPrefetch registers, one LDS read per MFMA.
         f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          constexpr int NSI = 2 * DS;
+          auto frag = [&](int i) { return row_frag<D>((i & 1) ? vt : kt, lane, x * 32, i >> 1); };
+          u32x4 fr[kPrefetch];
 #pragma unroll
-        for (int sl = 0; sl < DS; ++sl) {
-          s = mfma_32x32x16(row_frag<D>(kt, lane, x * 32, sl), qf[sl], s);
-          dp = mfma_32x32x16(row_frag<D>(vt, lane, x * 32, sl), dof[sl], dp);
+          for (int i = 0; i < kPrefetch; ++i) fr[i] = frag(i);
+#pragma unroll
+          for (int i = 0; i < NSI; ++i) {
+            const u32x4 a = fr[i % kPrefetch];
+            if (i + kPrefetch < NSI) fr[i % kPrefetch] = frag(i + kPrefetch);
+            if (i & 1) dp = mfma_32x32x16(a, dof[i >> 1], dp);
+            else s = mfma_32x32x16(a, qf[i >> 1], s);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPrefetch, 0);
+#pragma unroll
+          for (int i = 0; i < NSI - kPrefetch; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
         }
         float ds[16];
 #pragma unroll
