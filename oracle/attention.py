@@ -13,7 +13,8 @@ only as dense linear-algebra and elementwise primitives:
     P_ij  = exp(s_ij - LSE_i)  (0 outside A(i))
     O_i   = sum_j P_ij v_j
 
-with A(i) = {0..N-1} (non-causal) or {0..i} (causal), and the textbook softmax
+with A(i) = {0..N-1} (non-causal) or {0..i} (causal), optionally narrowed to a
+sliding window of w keys on each side, |i - j| <= w, and the textbook softmax
 Jacobian for the backward:
 
     dP_ij = dO_i . v_j
@@ -32,7 +33,9 @@ Sources, by page title and section:
   * [LONGCTX] "6.1 2023 年代：長上下文擴展技術：FlashAttention、RoPE 與稀疏注意力"
       (cccbook): §2.2 (分塊與重計算) -- the forward keeps the output and the
       per-row log-sum-exp statistic; §2.3 -- the result is exact, identical to
-      standard softmax attention.
+      standard softmax attention; §4 (稀疏注意力與線性注意力) -- sliding-window
+      attention, where each query sees only a fixed number of tokens before and
+      after it.
   * [LA2] "Lightning Attention-2 新一代注意力机制": the mask of a
       unidirectional (GPT-style) model is lower triangular.
 
@@ -42,6 +45,10 @@ Readings where the pages leave a step open:
     on future keys, contradicting the "no future information" use in [EVOL] §6;
   * causal alignment is j <= i with one sequence length for queries and keys,
     so no row is ever fully masked;
+  * a window w counts keys on each side of the query, excluding the query
+    itself: A(i) narrows to i - w <= j <= i + w, intersected with j <= i under
+    the causal mask; w = 0 leaves the query's own key only, w >= N - 1 changes
+    nothing, and no row is ever empty;
   * LSE is the natural log over the *scaled* scores, masked keys excluded;
   * head h of the query reads K/V head floor(h / G), G = H_q / H_kv
     (contiguous groups);
@@ -100,8 +107,14 @@ def _shapes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool):
     return B, Hq, Hkv, N, d, Hq // Hkv
 
 
+def _check_window(window: Optional[int]) -> None:
+    if window is not None and int(window) < 0:
+        raise ValueError("window must be >= 0 (or None for no window)")
+
+
 def _row_probs(q_rows: torch.Tensor, k_head: torch.Tensor, rows: torch.Tensor,
-               causal: bool, scale: float) -> Tuple[torch.Tensor, torch.Tensor]:
+               causal: bool, scale: float,
+               window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Scores -> (P, LSE) for a set of query rows of one head, over all keys.
 
     q_rows [R, d], k_head [N, d], rows [R] = the query positions i of q_rows.
@@ -109,10 +122,13 @@ def _row_probs(q_rows: torch.Tensor, k_head: torch.Tensor, rows: torch.Tensor,
     """
     N = k_head.shape[0]
     s = scale * (q_rows @ k_head.transpose(0, 1))              # s_ij, [R, N]
+    keys = torch.arange(N, dtype=torch.int64)
     if causal:
-        keys = torch.arange(N, dtype=torch.int64)
         s = s.masked_fill(keys[None, :] > rows[:, None], -math.inf)
-    m = s.max(dim=1).values                                    # finite: key 0 is always in A(i)
+    if window is not None:
+        dist = keys[None, :] - rows[:, None]                   # j - i
+        s = s.masked_fill((dist < -int(window)) | (dist > int(window)), -math.inf)
+    m = s.max(dim=1).values                                    # finite: key i is always in A(i)
     ell = torch.exp(s - m[:, None]).sum(dim=1)
     lse = m + torch.log(ell)
     p = torch.exp(s - lse[:, None])                            # exp(-inf) = 0 on masked keys
@@ -120,8 +136,10 @@ def _row_probs(q_rows: torch.Tensor, k_head: torch.Tensor, rows: torch.Tensor,
 
 
 def attention_forward(q, k, v, causal: bool, scale: Optional[float] = None,
-                      row_block: int = _ROW_BLOCK) -> Tuple[torch.Tensor, torch.Tensor]:
+                      row_block: int = _ROW_BLOCK,
+                      window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """O [B,H_q,N,d] and LSE [B,H_q,N], both float64."""
+    _check_window(window)
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
     B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal)
     tau = default_scale(d) if scale is None else float(scale)
@@ -133,14 +151,16 @@ def attention_forward(q, k, v, causal: bool, scale: Optional[float] = None,
             for r0 in range(0, N, row_block):
                 r1 = min(N, r0 + row_block)
                 rows = torch.arange(r0, r1, dtype=torch.int64)
-                p, l_blk = _row_probs(q[b, h, r0:r1], k[b, g], rows, causal, tau)
+                p, l_blk = _row_probs(q[b, h, r0:r1], k[b, g], rows, causal, tau, window)
                 o[b, h, r0:r1] = p @ v[b, g]
                 lse[b, h, r0:r1] = l_blk
     return o, lse
 
 
-def attention_probs(q, k, causal: bool, scale: Optional[float] = None) -> torch.Tensor:
+def attention_probs(q, k, causal: bool, scale: Optional[float] = None,
+                    window: Optional[int] = None) -> torch.Tensor:
     """The full probability matrix P [B,H_q,N_q,N_k] (small inputs only)."""
+    _check_window(window)
     q, k = to_f64(q), to_f64(k)
     B, Hq, Hkv, N, d, G = _shapes(q, k, k, causal)
     tau = default_scale(d) if scale is None else float(scale)
@@ -148,12 +168,13 @@ def attention_probs(q, k, causal: bool, scale: Optional[float] = None) -> torch.
     rows = torch.arange(N, dtype=torch.int64)
     for b in range(B):
         for h in range(Hq):
-            out[b, h], _ = _row_probs(q[b, h], k[b, h // G], rows, causal, tau)
+            out[b, h], _ = _row_probs(q[b, h], k[b, h // G], rows, causal, tau, window)
     return out
 
 
 def forward_rows(q, k, v, causal: bool, scale: Optional[float], b: int, h: int,
-                 rows: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+                 rows: Sequence[int],
+                 window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """O and LSE of selected query rows of one (batch, query head).
 
     Used to check very large problems on sampled rows: each row is computed
@@ -164,15 +185,17 @@ def forward_rows(q, k, v, causal: bool, scale: Optional[float], b: int, h: int,
     d = q.shape[-1]
     tau = default_scale(d) if scale is None else float(scale)
     rows_t = torch.as_tensor(list(rows), dtype=torch.int64)
+    _check_window(window)
     q_r = to_f64(q[b, h])[rows_t]
     k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
-    p, lse = _row_probs(q_r, k_g, rows_t, causal, tau)
+    p, lse = _row_probs(q_r, k_g, rows_t, causal, tau, window)
     return p @ v_g, lse
 
 
 def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,
-                       row_block: int = _ROW_BLOCK):
+                       row_block: int = _ROW_BLOCK, window: Optional[int] = None):
     """dQ [B,H_q,N,d], dK and dV [B,H_kv,N,d] of L = sum(dO * O), float64."""
+    _check_window(window)
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
     B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal)
     if tuple(do.shape) != tuple(q.shape):
@@ -188,7 +211,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,
                 r1 = min(N, r0 + row_block)
                 rows = torch.arange(r0, r1, dtype=torch.int64)
                 q_blk, do_blk = q[b, h, r0:r1], do[b, h, r0:r1]
-                p, _ = _row_probs(q_blk, k[b, g], rows, causal, tau)
+                p, _ = _row_probs(q_blk, k[b, g], rows, causal, tau, window)
                 dp = do_blk @ v[b, g].transpose(0, 1)          # dP_ij = dO_i . v_j
                 c = (p * dp).sum(dim=1)                        # c_i = sum_k P_ik dP_ik
                 ds = p * (dp - c[:, None])                     # dS_ij
@@ -199,7 +222,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,
 
 
 def backward_dq_rows(q, k, v, do, causal: bool, scale: Optional[float], b: int,
-                     h: int, rows: Sequence[int]) -> torch.Tensor:
+                     h: int, rows: Sequence[int], window: Optional[int] = None) -> torch.Tensor:
     """dQ of selected query rows of one (batch, query head).
 
     dQ_i needs only row i of P and dP, so sampled rows of a large problem can
@@ -210,10 +233,11 @@ def backward_dq_rows(q, k, v, do, causal: bool, scale: Optional[float], b: int,
     d = q.shape[-1]
     tau = default_scale(d) if scale is None else float(scale)
     rows_t = torch.as_tensor(list(rows), dtype=torch.int64)
+    _check_window(window)
     q_r = to_f64(q[b, h])[rows_t]
     do_r = to_f64(do[b, h])[rows_t]
     k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
-    p, _ = _row_probs(q_r, k_g, rows_t, causal, tau)
+    p, _ = _row_probs(q_r, k_g, rows_t, causal, tau, window)
     dp = do_r @ v_g.transpose(0, 1)
     c = (p * dp).sum(dim=1)
     ds = p * (dp - c[:, None])

@@ -10,7 +10,8 @@ It follows the same definitions, from the pages named in
 ``oracle/attention.py``: scaled dot-product softmax attention
 ([EVOL] §2, "从“算力黑洞”到“效率革命”：大模型Attention的演进之路"), causal keys
 j <= i ([EVOL] §6), K/V head floor(h/G) for grouped queries ([EVOL] §3), the
-natural-log log-sum-exp statistic ([LONGCTX] §2.2, cccbook ch. 6.1), and the
+natural-log log-sum-exp statistic ([LONGCTX] §2.2, cccbook ch. 6.1), the
+sliding window of w keys on each side of a query ([LONGCTX] §4), and the
 analytic softmax gradients.  Only use it for N * N * d up to ~10^5.
 """
 from __future__ import annotations
@@ -28,15 +29,23 @@ def tolist4(x) -> List:
     return [[[[float(e) for e in row] for row in head] for head in bat] for bat in x]
 
 
-def _visible(i: int, n: int, causal: bool) -> List[int]:
-    return list(range(i + 1)) if causal else list(range(n))
+def _visible(i: int, n: int, causal: bool, window=None) -> List[int]:
+    """Key positions query i attends to, in increasing order."""
+    out = []
+    for j in range(n):
+        if causal and j > i:
+            continue
+        if window is not None and abs(i - j) > window:
+            continue
+        out.append(j)
+    return out
 
 
 def _dot(a: List[float], b: List[float]) -> float:
     return math.fsum(x * y for x, y in zip(a, b))
 
 
-def bf_forward(q, k, v, causal: bool, scale: float):
+def bf_forward(q, k, v, causal: bool, scale: float, window=None):
     """Returns (O, LSE) as nested lists: O[b][h][i][t], LSE[b][h][i]."""
     q, k, v = tolist4(q), tolist4(k), tolist4(v)
     B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -48,7 +57,7 @@ def bf_forward(q, k, v, causal: bool, scale: float):
         for h in range(Hq):
             g = h // G
             for i in range(N):
-                keys = _visible(i, N, causal)
+                keys = _visible(i, N, causal, window)
                 s = [scale * _dot(q[b][h][i], k[b][g][j]) for j in keys]
                 m = max(s)
                 lse = m + math.log(math.fsum(math.exp(x - m) for x in s))
@@ -59,7 +68,7 @@ def bf_forward(q, k, v, causal: bool, scale: float):
     return O, L
 
 
-def bf_backward(q, k, v, do, causal: bool, scale: float):
+def bf_backward(q, k, v, do, causal: bool, scale: float, window=None):
     """Returns (dQ, dK, dV) as nested lists for L = sum_{b,h,i,t} dO * O."""
     q, k, v, do = tolist4(q), tolist4(k), tolist4(v), tolist4(do)
     B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -73,7 +82,7 @@ def bf_backward(q, k, v, do, causal: bool, scale: float):
         for h in range(Hq):
             g = h // G
             for i in range(N):
-                keys = _visible(i, N, causal)
+                keys = _visible(i, N, causal, window)
                 s = [scale * _dot(q[b][h][i], k[b][g][j]) for j in keys]
                 m = max(s)
                 lse = m + math.log(math.fsum(math.exp(x - m) for x in s))

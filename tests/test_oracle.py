@@ -319,3 +319,89 @@ def test_row_blocking_does_not_change_results():
         gb = attention_backward(q, k, v, do, causal, row_block=512)
         for x, y in zip(ga, gb):
             assert torch.allclose(x, y, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# sliding window ([LONGCTX] §4): keys with |i - j| <= w, intersected with the
+# causal mask
+# --------------------------------------------------------------------------
+WINDOWS = [0, 1, 2, 5, 8, 40]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window", WINDOWS)
+def test_window_forward_matches_bruteforce(window, causal):
+    B, Hq, Hkv, N, d = 2, 4, 2, 17, 8
+    q, k, v = rnd(40, B, Hq, N, d), rnd(41, B, Hkv, N, d), rnd(42, B, Hkv, N, d)
+    o, lse = attention_forward(q, k, v, causal, 0.41, row_block=5, window=window)
+    bo, bl = bf_forward(q, k, v, causal, 0.41, window=window)
+    assert max_rel(o, bo) < 1e-12 and max_rel(lse, bl) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window", [0, 1, 3, 11])
+def test_window_backward_matches_bruteforce(window, causal):
+    B, Hq, Hkv, N, d = 1, 4, 2, 12, 4
+    q, k, v = rnd(43, B, Hq, N, d), rnd(44, B, Hkv, N, d), rnd(45, B, Hkv, N, d)
+    do = rnd(46, B, Hq, N, d)
+    dq, dk, dv = attention_backward(q, k, v, do, causal, 0.29, row_block=5, window=window)
+    bq, bk, bv = bf_backward(q, k, v, do, causal, 0.29, window=window)
+    assert max_rel(dq, bq) < 1e-11 and max_rel(dk, bk) < 1e-11 and max_rel(dv, bv) < 1e-11
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_zero_is_identity(causal):
+    """w = 0: every query sees only its own key, so O_i = v_i and LSE_i = tau q_i.k_i;
+    P_ii = 1 makes dS = 0 (dQ = dK = 0) and dV_i the sum of dO_i over the group."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 10, 6
+    q, k, v = rnd(47, B, Hq, N, d), rnd(48, B, Hkv, N, d), rnd(49, B, Hkv, N, d)
+    do = rnd(50, B, Hq, N, d)
+    tau = 0.7
+    o, lse = attention_forward(q, k, v, causal, tau, window=0)
+    G = Hq // Hkv
+    for h in range(Hq):
+        assert torch.allclose(o[0, h], v[0, h // G], rtol=0, atol=1e-15)
+        assert torch.allclose(lse[0, h], tau * (q[0, h] * k[0, h // G]).sum(-1), rtol=0, atol=1e-14)
+    dq, dk, dv = attention_backward(q, k, v, do, causal, tau, window=0)
+    assert float(dq.abs().max()) < 1e-14 and float(dk.abs().max()) < 1e-14
+    want_dv = do.reshape(B, Hkv, G, N, d).sum(2)
+    assert torch.allclose(dv, want_dv, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_window_covering_everything_changes_nothing(causal):
+    B, Hq, Hkv, N, d = 1, 2, 1, 23, 8
+    q, k, v = rnd(51, B, Hq, N, d), rnd(52, B, Hkv, N, d), rnd(53, B, Hkv, N, d)
+    o0, l0 = attention_forward(q, k, v, causal)
+    for w in (N - 1, N, 10 * N):
+        o, l = attention_forward(q, k, v, causal, window=w)
+        assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
+def test_noncausal_window_is_symmetric_under_reversal():
+    """The band |i - j| <= w is symmetric: reversing the sequence order of Q, K
+    and V reverses the output rows (a causal mask would not survive this)."""
+    B, Hq, Hkv, N, d = 1, 2, 2, 19, 8
+    q, k, v = rnd(54, B, Hq, N, d), rnd(55, B, Hkv, N, d), rnd(56, B, Hkv, N, d)
+    o, lse = attention_forward(q, k, v, False, window=4)
+    o_r, lse_r = attention_forward(q.flip(2), k.flip(2), v.flip(2), False, window=4)
+    assert torch.allclose(o_r.flip(2), o, atol=1e-13) and torch.allclose(lse_r.flip(2), lse, atol=1e-13)
+
+
+def test_window_row_samplers_match_full():
+    B, Hq, Hkv, N, d = 1, 2, 1, 50, 8
+    q, k, v = rnd(57, B, Hq, N, d), rnd(58, B, Hkv, N, d), rnd(59, B, Hkv, N, d)
+    do = rnd(60, B, Hq, N, d)
+    o, lse = attention_forward(q, k, v, True, window=7)
+    dq, _, _ = attention_backward(q, k, v, do, True, window=7)
+    rows = [0, 3, 7, 8, 30, 49]
+    ro, rl = forward_rows(q, k, v, True, None, 0, 1, rows, window=7)
+    rq = backward_dq_rows(q, k, v, do, True, None, 0, 1, rows, window=7)
+    assert torch.allclose(ro, o[0, 1, rows], atol=1e-14) and torch.allclose(rl, lse[0, 1, rows], atol=1e-14)
+    assert torch.allclose(rq, dq[0, 1, rows], atol=1e-14)
+
+
+def test_negative_window_is_rejected():
+    q = rnd(61, 1, 1, 4, 4)
+    with pytest.raises(ValueError):
+        attention_forward(q, q, q, True, window=-1)

@@ -35,6 +35,10 @@ MUTANTS = {
     "dp_uses_k": ("dp = do_blk @ v[b, g].transpose(0, 1)          # dP_ij", "dp = do_blk @ k[b, g].transpose(0, 1)          # dP_ij"),
     "dk_overwrites_group": ("dk[b, g] += tau", "dk[b, g] = tau"),
     "o_uses_k": ("o[b, h, r0:r1] = p @ v[b, g]", "o[b, h, r0:r1] = p @ k[b, g]"),
+    "window_off_by_one_left": ("(dist < -int(window))", "(dist <= -int(window))"),
+    "window_off_by_one_right": ("(dist > int(window))", "(dist >= int(window))"),
+    "window_left_side_only": ("(dist < -int(window)) | (dist > int(window))", "(dist < -int(window))"),
+    "window_ignored": ("if window is not None:\n        dist", "if False:\n        dist"),
 }
 
 
@@ -72,6 +76,12 @@ def pins_pass(mod) -> bool:
             bg = bf_backward(q, k, v, do, causal, 0.37)
             for x, y in zip(g, bg):
                 if not torch.allclose(x, torch.tensor(y, dtype=torch.float64), atol=1e-10):
+                    return False
+            for w in (0, 2):
+                o, lse = mod.attention_forward(q, k, v, causal, 0.37, row_block=4, window=w)
+                bo, bl = bf_forward(q, k, v, causal, 0.37, window=w)
+                if not (torch.allclose(o, torch.tensor(bo, dtype=torch.float64), atol=1e-11)
+                        and torch.allclose(lse, torch.tensor(bl, dtype=torch.float64), atol=1e-11)):
                     return False
     except Exception:
         return False
