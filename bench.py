@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s (causal bf16, d=128) at N=8K–32K; % of MFMA bf16 peak"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
-BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K")
+BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K")
 
 
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
@@ -157,11 +157,11 @@ def cpu_baseline(w, x, n_heads):
     q, k, v = sl("q", hq), sl("k", hk), sl("v", hk)
     threads = torch.get_num_threads()
     t0 = time.perf_counter()
-    attention_forward(q, k, v, True)
-    pairs = hq * w.N * (w.N + 1) // 2
+    attention_forward(q, k, v, True, window=w.window)
+    pairs = hq * w.keys_per_query(True)
     flops = 4 * w.d * pairs
     if w.with_grad:
-        attention_backward(q, k, v, sl("do", hq), True)
+        attention_backward(q, k, v, sl("do", hq), True, window=w.window)
         flops += 10 * w.d * pairs
     dt = time.perf_counter() - t0
     what = "forward + backward" if w.with_grad else "forward"
@@ -232,13 +232,13 @@ def main():
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream)
+        attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream, window=w.window)
         mark(1)
         if w.with_grad:
             attn.bwd_preprocess(o, do, delta, stream=stream)
             mark(2)
             attn.bwd_grads(q, k, v, do, lse, delta, causal=True, dq=dq, dk=dk, dv=dv,
-                           stream=stream)
+                           stream=stream, window=w.window)
             mark(3)
 
     if args.copy_calibration_mib > 0:
@@ -311,13 +311,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": True, "pass": "fwd+bwd" if w.with_grad else "fwd",
-                   "flops_per_step": step_flops, "seed": w.seed, "input_scale": w.in_scale},
+                   "flops_per_step": step_flops, "seed": w.seed, "input_scale": w.in_scale,
+                   "window": w.window},
         "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
         "parts": parts,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64}[w.name]
+        default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1}[w.name]
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_heads or default_heads)
     print(json.dumps(result), flush=True)
 

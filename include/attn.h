@@ -143,6 +143,29 @@ int attn_bwd_grads(const void* q, const void* k, const void* v, const void* dout
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                    void* stream);
 
+/*
+ * Sliding-window attention (page "6.1 2023 年代：長上下文擴展技術：FlashAttention、
+ * RoPE 與稀疏注意力", §4): query i attends to key j only when |i - j| <= window,
+ * intersected with j <= i when causal != 0.  window counts keys on each side,
+ * the query's own key excluded: window = 0 leaves only key i, window >= N - 1
+ * gives exactly the plain call.  Arguments, layouts, ownership and errors are
+ * those of attn_fwd / attn_bwd / attn_bwd_grads, plus ATTN_ERR_SHAPE for
+ * window < 0.  Tiles of keys outside every row's band are neither loaded nor
+ * computed, so the work grows with N * window instead of N^2.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                    float scale, void* stream);
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes,
+                    int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                    float scale, void* stream);
+int attn_bwd_grads_window(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                          float scale, void* stream);
+
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
  * of the last failure on the calling thread.  Never NULL. */
 const char* attn_strerror(int code);

@@ -27,7 +27,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads", "attn_strerror",
-            "attn_device_check")
+            "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window")
 
 ATTN_OK = 0
 
@@ -63,6 +63,12 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_dq.restype = i
     L.attn_bwd_grads.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.attn_bwd_grads.restype = i
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_window.restype = i
+    L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    L.attn_bwd_window.restype = i
+    L.attn_bwd_grads_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    L.attn_bwd_grads_window.restype = i
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_strerror.argtypes = [i]
@@ -111,8 +117,12 @@ def _dims(q: torch.Tensor, k: torch.Tensor) -> Tuple[int, int, int, int, int]:
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
         scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-        lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """O = softmax(scale*QK^T + mask)V (bf16) and LSE (fp32 [B,Hq,N]) on the GPU."""
+        lse: Optional[torch.Tensor] = None, stream=None,
+        window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O = softmax(scale*QK^T + mask)V (bf16) and LSE (fp32 [B,Hq,N]) on the GPU.
+
+    window: None, or the sliding window (keys with |i - j| <= window).
+    """
     B, Hq, Hkv, N, d = _dims(q, k)
     _check_bf16("q", q, (B, Hq, N, d))
     _check_bf16("k", k, (B, Hkv, N, d))
@@ -126,10 +136,15 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                        B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    if window is None:
+        rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                            B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    else:
+        rc = lib().attn_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                   B, Hq, Hkv, N, d, int(bool(causal)), int(window), tau,
+                                   _stream(stream))
     if rc != ATTN_OK:
-        raise AttnError(rc, "attn_fwd")
+        raise AttnError(rc, "attn_fwd" if window is None else "attn_fwd_window")
     return out, lse
 
 
@@ -138,8 +153,11 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
         dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None,
-        stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """dQ, dK, dV (bf16) of L = sum(dO * O), recomputing scores from the LSE."""
+        stream=None, window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV (bf16) of L = sum(dO * O), recomputing scores from the LSE.
+
+    window: None, or the sliding window the forward used.
+    """
     B, Hq, Hkv, N, d = _dims(q, k)
     for name, t, shp in (("q", q, (B, Hq, N, d)), ("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
                          ("o", o, (B, Hq, N, d)), ("do", do, (B, Hq, N, d))):
@@ -153,11 +171,18 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if window is None:
+        rc = lib().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                            B, Hq, Hkv, N, d, int(bool(causal)), tau, _stream(stream))
+    else:
+        rc = lib().attn_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                                   B, Hq, Hkv, N, d, int(bool(causal)), int(window), tau,
+                                   _stream(stream))
     if rc != ATTN_OK:
-        raise AttnError(rc, "attn_bwd")
+        raise AttnError(rc, "attn_bwd" if window is None else "attn_bwd_window")
     return dq, dk, dv
 
 
@@ -224,8 +249,8 @@ def bwd_dq(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[float] 
 
 def bwd_grads(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[float] = None,
               dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-              dv: Optional[torch.Tensor] = None,
-              stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+              dv: Optional[torch.Tensor] = None, stream=None,
+              window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """dQ, dK, dV (bf16) in one launch: what bwd_dkdv and bwd_dq give, bitwise."""
     B, Hq, Hkv, N, d = _stage_checks(q, k, v, do, lse, delta)
     dq = torch.empty_like(q) if dq is None else dq
@@ -235,9 +260,15 @@ def bwd_grads(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[floa
     _check_bf16("dk", dk, (B, Hkv, N, d))
     _check_bf16("dv", dv, (B, Hkv, N, d))
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    rc = lib().attn_bwd_grads(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
-                              _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
-                              int(bool(causal)), tau, _stream(stream))
+    if window is None:
+        rc = lib().attn_bwd_grads(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d,
+                                  int(bool(causal)), tau, _stream(stream))
+    else:
+        rc = lib().attn_bwd_grads_window(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                                         _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv,
+                                         N, d, int(bool(causal)), int(window), tau,
+                                         _stream(stream))
     if rc != ATTN_OK:
-        raise AttnError(rc, "attn_bwd_grads")
+        raise AttnError(rc, "attn_bwd_grads" if window is None else "attn_bwd_grads_window")
     return dq, dk, dv

@@ -74,11 +74,12 @@ int current_device_check() {
   return device_check_impl(dev);
 }
 
-}  // namespace
+int check_window(int window) { return window >= 0 ? ATTN_OK : ATTN_ERR_SHAPE; }
 
-ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                         void* stream) {
+// window < 0: no window (the plain entry points); >= 0: checked by callers.
+int fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int N, int d, int causal, int window, float scale, void* stream,
+             const char* where) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   int rc = check_problem(B, Hq, Hkv, N, d);
   if (rc) return rc;
@@ -86,20 +87,15 @@ ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, f
     return ATTN_ERR_UNSUPPORTED;
   if ((rc = check_scale(scale))) return rc;
   if ((rc = current_device_check())) return rc;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, scale};
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal != 0, scale, window};
   hipError_t e = attn::launch_fwd(a, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd launch");
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, where);
 }
 
-ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
-  if (check_problem(B, Hq, Hkv, N, d)) return 0;
-  return attn::bwd_workspace_bytes(B, Hq, N);
-}
-
-ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                         void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                         int N, int d, int causal, float scale, void* stream) {
+int bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+             int window, float scale, void* stream, const char* where) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return ATTN_ERR_NULL;
   int rc = check_problem(B, Hq, Hkv, N, d);
@@ -111,9 +107,48 @@ ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void
   if ((rc = check_scale(scale))) return rc;
   if ((rc = current_device_check())) return rc;
   attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace,
-                  B, Hq, Hkv, N, d, causal != 0, scale};
+                  B, Hq, Hkv, N, d, causal != 0, scale, window};
   hipError_t e = attn::launch_bwd(a, (hipStream_t)stream);
-  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd launch");
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, where);
+}
+
+}  // namespace
+
+ATTN_EXPORT int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, -1, scale, stream,
+                  "attn_fwd launch");
+}
+
+ATTN_EXPORT int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                                float scale, void* stream) {
+  if (check_window(window)) return ATTN_ERR_SHAPE;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream,
+                  "attn_fwd_window launch");
+}
+
+ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  if (check_problem(B, Hq, Hkv, N, d)) return 0;
+  return attn::bwd_workspace_bytes(B, Hq, N);
+}
+
+ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                         int N, int d, int causal, float scale, void* stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
+                  d, causal, -1, scale, stream, "attn_bwd launch");
+}
+
+ATTN_EXPORT int attn_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                                int N, int d, int causal, int window, float scale, void* stream) {
+  if (check_window(window)) return ATTN_ERR_SHAPE;
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N,
+                  d, causal, window, scale, stream, "attn_bwd_window launch");
 }
 
 ATTN_EXPORT int attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int Hq,
@@ -179,6 +214,20 @@ ATTN_EXPORT int attn_bwd_grads(const void* q, const void* k, const void* v, cons
                   B, Hq, Hkv, N, d, causal != 0, scale};
   hipError_t e = attn::launch_bwd_grads(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_grads launch");
+}
+
+ATTN_EXPORT int attn_bwd_grads_window(const void* q, const void* k, const void* v,
+                                      const void* dout, const float* lse, const float* delta,
+                                      void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                                      int N, int d, int causal, int window, float scale,
+                                      void* stream) {
+  if (check_window(window)) return ATTN_ERR_SHAPE;
+  int rc = check_stage(q, k, v, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, N, d, scale);
+  if (rc) return rc;
+  attn::BwdArgs a{q, k, v, nullptr, lse, dout, dq, dk, dv, (float*)delta,
+                  B, Hq, Hkv, N, d, causal != 0, scale, window};
+  hipError_t e = attn::launch_bwd_grads(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_grads_window launch");
 }
 
 ATTN_EXPORT const char* attn_strerror(int code) {

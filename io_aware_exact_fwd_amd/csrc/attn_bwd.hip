@@ -77,13 +77,14 @@ struct DkdvCfg {
   static_assert(kRedBytes <= kLdsBytes, "reduction fits in the tile memory");
 };
 
-// One dK/dV workgroup: w is its index in the dK/dV grid, smem its LDS.
-template <int D, int NWK, bool CAUSAL>
+// One dK/dV workgroup: w is its index in the dK/dV grid, smem its LDS.  With
+// LOCAL, query i sees key j only when |i - j| <= window.
+template <int D, int NWK, bool CAUSAL, bool LOCAL>
 __device__ __forceinline__ void dkdv_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
-    float scale, float scale_log2, int xcd_remap, int w, unsigned char* smem) {
+    float scale, float scale_log2, int xcd_remap, int window, int w, unsigned char* smem) {
   using C = DkdvCfg<D, NWK>;
   constexpr int kPrefetch = 3;   // (A, B) fragment pairs in flight ahead of their MFMA
   constexpr int NW = C::kNW;
@@ -119,8 +120,11 @@ __device__ __forceinline__ void dkdv_block(
   auto stats = [&](int buf) { return (float*)(smem + C::kStats + buf * 2 * BQ * 4); };
 
   const int n_qt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? k0 / BQ : 0;            // first query tile that sees these keys
-  const int per_head = n_qt - qt0;
+  // query tiles [qt0, qt_end) hold every query that sees one of these keys
+  const int q_first = CAUSAL ? k0 : (LOCAL ? max(0, k0 - window) : 0);
+  const int qt0 = q_first / BQ;
+  const int qt_end = LOCAL ? min(n_qt, (k0 + C::kBKV + window + BQ - 1) / BQ) : n_qt;
+  const int per_head = qt_end - qt0;
   const int n_iter = per_head * G;
 
   // the query tile of iteration it is (head hk*G + it / per_head, tile
@@ -175,14 +179,16 @@ __device__ __forceinline__ void dkdv_block(
     const int buf = it & 1;
     const int qs = qt_n * BQ + 32 * qh;   // first query row of this wave in tile it
     if (it + 1 < n_iter) {
-      if (++qt_n == n_qt) {
+      if (++qt_n == qt_end) {
         qt_n = qt0;
         ++hh_n;
       }
       issue(hh_n, qt_n, buf ^ 1);
       load_stats(hh_n, qt_n);
     }
-    if (kw0 < N && !(CAUSAL && qs + 31 < kw0)) {
+    // the wave's 32 queries and 32 keys share at least one visible pair
+    const bool in_band = !LOCAL || (qs <= kw0 + 31 + window && (CAUSAL || qs + 31 >= kw0 - window));
+    if (kw0 < N && !(CAUSAL && qs + 31 < kw0) && in_band) {
       const unsigned char* Qt = qtile(buf);
       const unsigned char* dOt = Qt + C::kQTile;
       const float* lse_l = stats(buf);
@@ -222,7 +228,8 @@ __device__ __forceinline__ void dkdv_block(
       }
 
       // P = 2^(s*tau*log2e - LSE*log2e), dS = P (dP - D); rows 8r + 4hi + 0..3
-      const bool need_mask = CAUSAL && qs < kw0 + 31;
+      const bool need_mask = (CAUSAL && qs < kw0 + 31) ||
+                             (LOCAL && (qs + 31 > kw0 + window || (!CAUSAL && qs < kw0 + 31 - window)));
       const int key = kw0 + l32;
       float p[16], ds[16];
 #pragma unroll
@@ -233,7 +240,11 @@ __device__ __forceinline__ void dkdv_block(
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * r + e;
           float pv = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lv[e]));
-          if (need_mask && key > qs + 8 * r + 4 * hi + e) pv = 0.f;
+          if (need_mask) {
+            const int q = qs + 8 * r + 4 * hi + e;
+            if ((CAUSAL && key > q) || (LOCAL && (key < q - window || (!CAUSAL && key > q + window))))
+              pv = 0.f;
+          }
           p[i] = pv;
           ds[i] = pv * (dp[i] - dv[e]);
         }
@@ -296,16 +307,16 @@ __device__ __forceinline__ void dkdv_block(
   }
 }
 
-template <int D, int NWK, int WPE, bool CAUSAL>
+template <int D, int NWK, int WPE, bool CAUSAL, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
-    float scale, float scale_log2, int xcd_remap) {
+    float scale, float scale_log2, int xcd_remap, int window) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  dkdv_block<D, NWK, CAUSAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale, scale_log2,
-                             xcd_remap, blockIdx.x, smem);
+  dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
+                                    scale_log2, xcd_remap, window, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -319,13 +330,14 @@ struct DqCfg {
   static constexpr int kLdsBytes = 2 * 2 * kTile;   // double-buffered K and V
 };
 
-// One dQ workgroup: w is its index in the dQ grid, smem its LDS.
-template <int D, int BC, int NW, bool CAUSAL>
+// One dQ workgroup: w is its index in the dQ grid, smem its LDS.  With LOCAL,
+// query i sees key j only when |i - j| <= window.
+template <int D, int BC, int NW, bool CAUSAL, bool LOCAL>
 __device__ __forceinline__ void dq_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
-    float scale_log2, int xcd_remap, int w, unsigned char* smem) {
+    float scale_log2, int xcd_remap, int window, int w, unsigned char* smem) {
   using C = DqCfg<D, BC, NW>;
   constexpr int kPrefetch = 6;   // K/V fragments in flight ahead of their MFMA
   constexpr int DS = D / 16;
@@ -366,7 +378,10 @@ __device__ __forceinline__ void dq_block(
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqT[db] = f32x16{};
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : N;
+  // keys this workgroup's queries can see: [kv_begin, kv_end)
+  const int kv_begin = LOCAL ? max(0, q0 - window) : 0;
+  const int kv_end = CAUSAL ? min(N, q0 + C::kBQ) : (LOCAL ? min(N, q0 + C::kBQ + window) : N);
+  const int j_first = kv_begin / BC;
   const int n_tiles = (kv_end + BC - 1) / BC;
   TileLoader<D, BC, NW> ldk;
   ldk.init(wave, lane);
@@ -375,20 +390,28 @@ __device__ __forceinline__ void dq_block(
     ldk.load(K + kv_off, j * BC, N, kt, wave);
     ldk.load(V + kv_off, j * BC, N, kt + C::kTile, wave);
   };
-  issue_tile(0, 0);
+  issue_tile(j_first, j_first & 1);
   wait_all_memory();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // a key range [k_lo, k_hi] meets the band of this wave's 32 queries
+  auto meets_band = [&](int k_lo, int k_hi) {
+    return !LOCAL || (k_hi >= qw0 - window && (CAUSAL || k_lo <= qw0 + 31 + window));
+  };
+  for (int j = j_first; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int kstart = j * BC;
     if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
-    if (wave_live && (!CAUSAL || kstart <= qw0 + 31)) {
+    if (wave_live && (!CAUSAL || kstart <= qw0 + 31) && meets_band(kstart, kstart + BC - 1)) {
       const unsigned char* kt = smem + buf * 2 * C::kTile;
       const unsigned char* vt = kt + C::kTile;
-      const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0);
+      const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0) ||
+                             (LOCAL && (kstart < qw0 + 31 - window ||
+                                        (!CAUSAL && kstart + BC - 1 > qw0 + window)));
 #pragma unroll
       for (int x = 0; x < KB; ++x) {
+        // 32-key blocks outside every row's band are skipped (wave-uniform)
+        if (LOCAL && !meets_band(kstart + x * 32, kstart + x * 32 + 31)) continue;
         // S^T and dP^T: 32 keys x 32 queries, lane holds query column l%32
         // Step i reads slab i/2 of K (even i) or V (odd i); the fragments go
         // through a ring of kPrefetch registers, one LDS read per MFMA.
@@ -420,7 +443,9 @@ __device__ __forceinline__ void dq_block(
           float pv = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lse_l2));
           if (need_mask) {
             const int key = kstart + x * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key >= N || (CAUSAL && key > q)) pv = 0.f;
+            if (key >= N || (CAUSAL && key > q) ||
+                (LOCAL && (key < q - window || (!CAUSAL && key > q + window))))
+              pv = 0.f;
           }
           ds[i] = pv * (dp[i] - del);
         }
@@ -451,39 +476,39 @@ __device__ __forceinline__ void dq_block(
   }
 }
 
-template <int D, int BC, int NW, int WPE, bool CAUSAL>
+template <int D, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
-    float scale_log2, int xcd_remap) {
+    float scale_log2, int xcd_remap, int window) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
-  dq_block<D, BC, NW, CAUSAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale, scale_log2,
-                              xcd_remap, blockIdx.x, smem);
+  dq_block<D, BC, NW, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
+                                     scale_log2, xcd_remap, window, blockIdx.x, smem);
 }
 
 // dK/dV and dQ in one launch: workgroups [0, n_dkdv) are dK/dV blocks and the
 // rest dQ blocks.  The two halves are independent (both read only the inputs,
 // LSE and D), so dQ blocks fill the CUs that dK/dV blocks release instead of
 // waiting for the whole dK/dV grid to drain.  Both halves use 8 waves.
-template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL>
+template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void bwd_grads_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
     int BHkv, int BH, int Hq, int Hkv, int G, int n_dkdv, int n_qb, float scale, float scale_log2,
-    int xcd_kv, int xcd_q) {
+    int xcd_kv, int xcd_q, int window) {
   static_assert(2 * NWK == NW, "both halves run the same number of waves");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int w = blockIdx.x;
   if (w < n_dkdv)
-    dkdv_block<D, NWK, CAUSAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale, scale_log2,
-                               xcd_kv, w, smem);
+    dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
+                                      scale_log2, xcd_kv, window, w, smem);
   else
-    dq_block<D, BC, NW, CAUSAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
-                                scale_log2, xcd_q, w - n_dkdv, smem);
+    dq_block<D, BC, NW, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
+                                       scale_log2, xcd_q, window, w - n_dkdv, smem);
 }
 
 template <typename KernelT>
@@ -505,70 +530,89 @@ constexpr int kDkdvNWK = 4, kDkdvWPE = 2;
 // dQ: 8 waves x 32 queries, 128-key tiles (128 KB of double-buffered LDS).
 constexpr int kDqBC = 128, kDqNW = 8, kDqWPE = 2;
 
-template <int D, bool CAUSAL>
-hipError_t launch_dkdv_t(const BwdArgs& a, hipStream_t stream) {
-  using CK = DkdvCfg<D, kDkdvNWK>;
-  auto kern = bwd_dkdv_kernel<D, kDkdvNWK, kDkdvWPE, CAUSAL>;
-  static const hipError_t attr = allow_lds(kern, CK::kLdsBytes);
-  if (attr != hipSuccess) return attr;
-  const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
-  const int BHkv = a.B * a.Hkv;
-  const long long grid = (long long)BHkv * n_kb;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), CK::kLdsBytes, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                     a.N, BHkv, a.Hq, a.Hkv, a.Hq / a.Hkv, a.scale, a.scale * kLog2e,
-                     BHkv % 8 == 0 ? 1 : 0);
-  return hipGetLastError();
-}
+template <int D, bool CAUSAL, bool LOCAL>
+struct LaunchDkdv {
+  static hipError_t run(const BwdArgs& a, hipStream_t stream) {
+    using CK = DkdvCfg<D, kDkdvNWK>;
+    auto kern = bwd_dkdv_kernel<D, kDkdvNWK, kDkdvWPE, CAUSAL, LOCAL>;
+    static const hipError_t attr = allow_lds(kern, CK::kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
+    const int BHkv = a.B * a.Hkv;
+    const long long grid = (long long)BHkv * n_kb;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), CK::kLdsBytes, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                       a.N, BHkv, a.Hq, a.Hkv, a.Hq / a.Hkv, a.scale, a.scale * kLog2e,
+                       BHkv % 8 == 0 ? 1 : 0, a.window);
+    return hipGetLastError();
+  }
+};
 
-template <int D, bool CAUSAL>
-hipError_t launch_dq_t(const BwdArgs& a, hipStream_t stream) {
-  using CQ = DqCfg<D, kDqBC, kDqNW>;
-  auto kern = bwd_dq_kernel<D, kDqBC, kDqNW, kDqWPE, CAUSAL>;
-  static const hipError_t attr = allow_lds(kern, CQ::kLdsBytes);
-  if (attr != hipSuccess) return attr;
-  const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
-  const int BH = a.B * a.Hq;
-  const long long grid = (long long)BH * n_qb;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CQ::kThreads), CQ::kLdsBytes, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, BH, a.Hq,
-                     a.Hkv, a.Hq / a.Hkv, n_qb, a.scale, a.scale * kLog2e, BH % 8 == 0 ? 1 : 0);
-  return hipGetLastError();
-}
+template <int D, bool CAUSAL, bool LOCAL>
+struct LaunchDq {
+  static hipError_t run(const BwdArgs& a, hipStream_t stream) {
+    using CQ = DqCfg<D, kDqBC, kDqNW>;
+    auto kern = bwd_dq_kernel<D, kDqBC, kDqNW, kDqWPE, CAUSAL, LOCAL>;
+    static const hipError_t attr = allow_lds(kern, CQ::kLdsBytes);
+    if (attr != hipSuccess) return attr;
+    const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
+    const int BH = a.B * a.Hq;
+    const long long grid = (long long)BH * n_qb;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CQ::kThreads), CQ::kLdsBytes, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, BH, a.Hq,
+                       a.Hkv, a.Hq / a.Hkv, n_qb, a.scale, a.scale * kLog2e, BH % 8 == 0 ? 1 : 0,
+                       a.window);
+    return hipGetLastError();
+  }
+};
 
-template <int D, bool CAUSAL>
-hipError_t launch_grads_t(const BwdArgs& a, hipStream_t stream) {
-  using CK = DkdvCfg<D, kDkdvNWK>;
-  using CQ = DqCfg<D, kDqBC, kDqNW>;
-  static_assert(CK::kThreads == CQ::kThreads, "one workgroup size for both halves");
-  constexpr int lds = CK::kLdsBytes > CQ::kLdsBytes ? CK::kLdsBytes : CQ::kLdsBytes;
-  auto kern = bwd_grads_kernel<D, kDkdvNWK, kDqBC, kDqNW, kDqWPE, CAUSAL>;
-  static const hipError_t attr = allow_lds(kern, lds);
-  if (attr != hipSuccess) return attr;
-  const int BHkv = a.B * a.Hkv, BH = a.B * a.Hq;
-  const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
-  const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
-  const long long n_dkdv = (long long)BHkv * n_kb;
-  const long long grid = n_dkdv + (long long)BH * n_qb;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), lds, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,
-                     (uint16_t*)a.dv, a.N, BHkv, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, (int)n_dkdv, n_qb,
-                     a.scale, a.scale * kLog2e, BHkv % 8 == 0 ? 1 : 0, BH % 8 == 0 ? 1 : 0);
-  return hipGetLastError();
+template <int D, bool CAUSAL, bool LOCAL>
+struct LaunchGrads {
+  static hipError_t run(const BwdArgs& a, hipStream_t stream) {
+    using CK = DkdvCfg<D, kDkdvNWK>;
+    using CQ = DqCfg<D, kDqBC, kDqNW>;
+    static_assert(CK::kThreads == CQ::kThreads, "one workgroup size for both halves");
+    constexpr int lds = CK::kLdsBytes > CQ::kLdsBytes ? CK::kLdsBytes : CQ::kLdsBytes;
+    auto kern = bwd_grads_kernel<D, kDkdvNWK, kDqBC, kDqNW, kDqWPE, CAUSAL, LOCAL>;
+    static const hipError_t attr = allow_lds(kern, lds);
+    if (attr != hipSuccess) return attr;
+    const int BHkv = a.B * a.Hkv, BH = a.B * a.Hq;
+    const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
+    const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
+    const long long n_dkdv = (long long)BHkv * n_kb;
+    const long long grid = n_dkdv + (long long)BH * n_qb;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), lds, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,
+                       (uint16_t*)a.dv, a.N, BHkv, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, (int)n_dkdv,
+                       n_qb, a.scale, a.scale * kLog2e, BHkv % 8 == 0 ? 1 : 0,
+                       BH % 8 == 0 ? 1 : 0, a.window);
+    return hipGetLastError();
+  }
+};
+
+// (d, causal, window) -> kernel instance.  A window that covers every key
+// changes nothing and takes the plain kernels.
+template <template <int, bool, bool> class L>
+hipError_t dispatch(const BwdArgs& a, hipStream_t stream) {
+  const bool local = a.window >= 0 && a.window < a.N - 1;
+  if (a.d == 128) {
+    if (local) return a.causal ? L<128, true, true>::run(a, stream) : L<128, false, true>::run(a, stream);
+    return a.causal ? L<128, true, false>::run(a, stream) : L<128, false, false>::run(a, stream);
+  }
+  if (local) return a.causal ? L<64, true, true>::run(a, stream) : L<64, false, true>::run(a, stream);
+  return a.causal ? L<64, true, false>::run(a, stream) : L<64, false, false>::run(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 128)
-    return a.causal ? launch_grads_t<128, true>(a, stream) : launch_grads_t<128, false>(a, stream);
-  return a.causal ? launch_grads_t<64, true>(a, stream) : launch_grads_t<64, false>(a, stream);
+  return dispatch<LaunchGrads>(a, stream);
 }
 
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
@@ -576,15 +620,11 @@ hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 128)
-    return a.causal ? launch_dkdv_t<128, true>(a, stream) : launch_dkdv_t<128, false>(a, stream);
-  return a.causal ? launch_dkdv_t<64, true>(a, stream) : launch_dkdv_t<64, false>(a, stream);
+  return dispatch<LaunchDkdv>(a, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-  if (a.d == 128)
-    return a.causal ? launch_dq_t<128, true>(a, stream) : launch_dq_t<128, false>(a, stream);
-  return a.causal ? launch_dq_t<64, true>(a, stream) : launch_dq_t<64, false>(a, stream);
+  return dispatch<LaunchDq>(a, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {

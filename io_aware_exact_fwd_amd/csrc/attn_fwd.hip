@@ -27,6 +27,11 @@
 //   * causal: key tiles past a workgroup's last row are never loaded, a wave
 //     skips tiles past its own last row, and only tiles that cross the
 //     diagonal (or the ragged end of the sequence) evaluate the mask;
+//   * sliding window (page "6.1 … 長上下文擴展技術", §4): with LOCAL a query
+//     sees keys |i - j| <= window (and j <= i under the causal mask); key
+//     tiles outside the band of a workgroup are never loaded, a wave skips
+//     tiles outside its rows' bands, and only tiles that cross a band edge
+//     evaluate the mask;
 //   * exp is 2^x with scale*log2(e) folded into one FMA; the LSE is converted
 //     back to natural-log units of the scaled scores before it is stored;
 //   * workgroups run heaviest causal block first, and when B*Hq is a multiple
@@ -55,12 +60,13 @@ struct FwdCfg {
 // error (this matters for peaked rows).  LAG > 0 gives the same quotient
 // sum 2^(s-m) v / sum 2^(s-m) with factors bounded by 2^LAG, and skips most
 // rescales, at the cost of rounding that largest term too.
-template <int D, int BC, int NW, int WPE, bool CAUSAL, int LAG = 0>
+template <int D, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL, int LAG = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale_log2, int xcd_remap) {
+    int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale_log2, int xcd_remap,
+    int window) {
   using C = FwdCfg<D, BC, NW>;
   constexpr int kPrefetch = 6; // K fragments in flight ahead of their MFMA
   constexpr int DS = D / 16;   // k-slabs of the QK^T contraction
@@ -109,7 +115,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       qf[s] = row < N ? *(const u32x4*)(Qp + (size_t)row * D + s * 16 + 8 * hi) : zero4();
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::kBR) : N;
+  // keys this workgroup's rows can see: [kv_begin, kv_end)
+  const int kv_begin = LOCAL ? max(0, q0 - window) : 0;
+  const int kv_end = CAUSAL ? min(N, q0 + C::kBR) : (LOCAL ? min(N, q0 + C::kBR + window) : N);
+  const int j_first = kv_begin / BC;
   const int n_tiles = (kv_end + BC - 1) / BC;
 
   TileLoader<D, BC, NW> ldr;
@@ -126,16 +135,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  issue_tile(0, 0);
+  issue_tile(j_first, j_first & 1);
   wait_all_memory();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  for (int j = j_first; j < n_tiles; ++j) {
     const int buf = j & 1;
     const int kstart = j * BC;
     if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
 
-    if (wave_live && (!CAUSAL || kstart <= qw1)) {
+    // the tile meets this wave's band: some key in [qw0 - w, qw1 (+ w)]
+    const bool in_band = !LOCAL || (kstart + BC - 1 >= qw0 - window && (CAUSAL || kstart <= qw1 + window));
+    if (wave_live && (!CAUSAL || kstart <= qw1) && in_band) {
       const unsigned char* kt = smem + buf * 2 * C::kTile;
       const unsigned char* vt = kt + C::kTile;
 
@@ -167,8 +178,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
       }
 
-      // mask: only tiles that cross the diagonal or the ragged end
-      const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0);
+      // mask: only tiles that cross the diagonal, a band edge or the ragged end
+      const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0) ||
+                             (LOCAL && (kstart < qw1 - window || (!CAUSAL && kstart + BC - 1 > qw0 + window)));
       if (need_mask) {
         const int q = qw0 + l32;
 #pragma unroll
@@ -176,7 +188,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kstart + x * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key >= N || (CAUSAL && key > q)) s[x][i] = -INFINITY;
+            const bool out = key >= N || (CAUSAL && key > q) ||
+                             (LOCAL && (key < q - window || (!CAUSAL && key > q + window)));
+            if (out) s[x][i] = -INFINITY;
           }
       }
 
@@ -190,13 +204,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       const bool move = mx > m_run + (float)LAG;
       if (__any(move)) {
         const float m_new = move ? mx : m_run;
-        const float alpha = exp2_fast(m_run - m_new);   // 0 on the first tile
+        // 0 on a row's first visible tile.  With a window, rows of one wave can
+        // reach their band in different tiles; a row still at m_run = -inf
+        // that does not move keeps alpha = 1 (exp2(-inf - -inf) would be NaN).
+        const float alpha = (LOCAL && !move) ? 1.f : exp2_fast(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] *= alpha;
       }
-      // m_run is finite from the first visited tile on: key 0 is visible to every row
+      // Without a window m_run is finite from the first visited tile on (key 0
+      // is visible to every row).  With one, a row can meet a tile that is all
+      // outside its band before its first visible key; its m_run is still
+      // -inf and its exponentials are taken against 0 instead (all are 0).
+      const float m_ref = LOCAL && m_run == -INFINITY ? 0.f : m_run;
       u32x4 pf[KB][2];
       float lsum = 0.f;
 #pragma unroll
@@ -204,7 +225,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         float p[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = exp2_fast(__builtin_fmaf(s[x][i], scale_log2, -m_run));
+          p[i] = exp2_fast(__builtin_fmaf(s[x][i], scale_log2, -m_ref));
           lsum += p[i];
         }
         pf[x][0] = pack8(p);
@@ -247,14 +268,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   }
 }
 
-template <int D, int BC, int NW, int WPE, bool CAUSAL, int LAG = 0>
+template <int D, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL, int LAG = 0>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, BC, NW>;
   const int n_qb = (a.N + C::kBR - 1) / C::kBR;
   const int BH = a.B * a.Hq;
   const long long grid = (long long)BH * n_qb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  auto kern = attn_fwd_kernel<D, BC, NW, WPE, CAUSAL, LAG>;
+  auto kern = attn_fwd_kernel<D, BC, NW, WPE, CAUSAL, LOCAL, LAG>;
   // more than 64 KB of dynamic LDS has to be allowed once per kernel instance
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
@@ -263,7 +284,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, n_qb,
-                     a.scale * kLog2e, xcd_remap);
+                     a.scale * kLog2e, xcd_remap, a.window);
   return hipGetLastError();
 }
 
@@ -271,13 +292,22 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   // 8 waves x 32 rows = 256 query rows per workgroup, 128-key tiles (128 KB
-  // of double-buffered LDS: one workgroup per CU), two waves per SIMD.
+  // of double-buffered LDS: one workgroup per CU), two waves per SIMD.  A
+  // window that covers every key changes nothing and takes the plain kernel.
   constexpr int BC = 128, NW = 8, WPE = 2;
-  if (a.d == 128)
-    return a.causal ? launch_fwd_t<128, BC, NW, WPE, true>(a, stream)
-                    : launch_fwd_t<128, BC, NW, WPE, false>(a, stream);
-  return a.causal ? launch_fwd_t<64, BC, NW, WPE, true>(a, stream)
-                  : launch_fwd_t<64, BC, NW, WPE, false>(a, stream);
+  const bool local = a.window >= 0 && a.window < a.N - 1;
+  if (a.d == 128) {
+    if (local)
+      return a.causal ? launch_fwd_t<128, BC, NW, WPE, true, true>(a, stream)
+                      : launch_fwd_t<128, BC, NW, WPE, false, true>(a, stream);
+    return a.causal ? launch_fwd_t<128, BC, NW, WPE, true, false>(a, stream)
+                    : launch_fwd_t<128, BC, NW, WPE, false, false>(a, stream);
+  }
+  if (local)
+    return a.causal ? launch_fwd_t<64, BC, NW, WPE, true, true>(a, stream)
+                    : launch_fwd_t<64, BC, NW, WPE, false, true>(a, stream);
+  return a.causal ? launch_fwd_t<64, BC, NW, WPE, true, false>(a, stream)
+                  : launch_fwd_t<64, BC, NW, WPE, false, false>(a, stream);
 }
 
 }  // namespace attn

@@ -15,6 +15,7 @@ struct FwdArgs {
   int B, Hq, Hkv, N, d;
   bool causal;
   float scale;
+  int window = -1;  // sliding window: keys with |i - j| <= window; < 0 = none
 };
 
 struct BwdArgs {
@@ -31,6 +32,7 @@ struct BwdArgs {
   int B, Hq, Hkv, N, d;
   bool causal;
   float scale;
+  int window = -1;  // sliding window: keys with |i - j| <= window; < 0 = none
 };
 
 // Bytes of workspace the backward uses (fp32 D per query row).

@@ -49,6 +49,17 @@ class Workload:
     in_scale: float = 1.0
     with_grad: bool = False
     note: str = ""
+    window: Optional[int] = None    # sliding window |i - j| <= window, or none
+
+    def keys_per_query(self, causal: bool) -> int:
+        """Visible keys summed over the N query rows of one head (a count)."""
+        n, w = self.N, self.window
+        if w is None or w >= n - 1:
+            return n * (n + 1) // 2 if causal else n * n
+        left = (w + 1) * (w + 2) // 2 + (n - w - 1) * (w + 1)     # keys j in [i - w, i]
+        if causal:
+            return left
+        return 2 * left - n                                           # plus [i, i + w], i counted once
 
     @property
     def group(self) -> int:
@@ -56,8 +67,7 @@ class Workload:
 
     def pairs(self, causal: bool) -> int:
         """Unmasked (query, key) pairs over all (batch, query head)."""
-        per_head = self.N * (self.N + 1) // 2 if causal else self.N * self.N
-        return self.B * self.Hq * per_head
+        return self.B * self.Hq * self.keys_per_query(causal)
 
     def fwd_flops(self, causal: bool) -> int:
         """Algorithmic matmul FLOPs of the forward: 2d for QK^T plus 2d for PV."""
@@ -78,6 +88,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("fwd-8K", 1, 32, 32, 8192, 128, (True,), seed=2, in_scale=0.5),
         Workload("gqa-16K", 1, 64, 8, 16384, 128, (True,), seed=3),
         Workload("fb-32K", 1, 8, 8, 32768, 128, (True,), seed=4, with_grad=True),
+        Workload("swa-32K", 1, 8, 8, 32768, 128, (True,), seed=5, with_grad=True, window=4096,
+                 note="sliding-window causal attention, 4096 keys back"),
     )
 }
 

@@ -31,7 +31,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes",
                                            "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
                                            "attn_bwd_grads", "attn_strerror",
-                                           "attn_device_check"])
+                                           "attn_device_check", "attn_fwd_window",
+                                           "attn_bwd_window", "attn_bwd_grads_window"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -143,3 +144,20 @@ def test_valid_call_without_device_reports_hip_error(L):
     rc = fwd(L)
     assert rc in (3, 6)
     assert L.attn_device_check(0) in (3, 6)
+
+
+def test_window_entry_points_validate(L):
+    """Windowed calls: the plain calls' checks plus window >= 0, all before any
+    device work."""
+    # negative window
+    assert L.attn_fwd_window(A, A, A, A, A, 1, 2, 2, 16, 64, 1, -1, 0.1, None) == 2
+    assert L.attn_bwd_window(A, A, A, A, A, A, A, A, A, A, 1 << 20, 1, 2, 2, 16, 64, 1, -3, 0.1, None) == 2
+    assert L.attn_bwd_grads_window(*([A] * 9), 1, 2, 2, 16, 64, 1, -1, 0.1, None) == 2
+    # the plain checks still apply
+    assert L.attn_fwd_window(None, A, A, A, A, 1, 2, 2, 16, 64, 1, 4, 0.1, None) == 1
+    assert L.attn_fwd_window(A, A, A, A, A, 1, 3, 2, 16, 64, 1, 4, 0.1, None) == 2
+    assert L.attn_fwd_window(A, A, A, A, A, 1, 2, 2, 16, 96, 1, 4, 0.1, None) == 3
+    assert L.attn_fwd_window(A, A, A, A, A, 1, 2, 2, 16, 64, 1, 4, 0.0, None) == 5
+    assert L.attn_bwd_window(A, A, A, A, A, A, A, A, A, A, 0, 1, 2, 2, 16, 64, 1, 4, 0.1, None) == 4
+    assert L.attn_bwd_grads_window(*([A] * 8), MIS, 1, 2, 2, 16, 64, 1, 4, 0.1, None) == 3
+
