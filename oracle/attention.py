@@ -49,6 +49,11 @@ Readings where the pages leave a step open:
     itself: A(i) narrows to i - w <= j <= i + w, intersected with j <= i under
     the causal mask; w = 0 leaves the query's own key only, w >= N - 1 changes
     nothing, and no row is ever empty;
+  * with fewer queries than keys (N_q < N_k: decoding against a KV cache, the
+    setting of [EVOL] §1 and §3 and [LONGCTX] §1.5) the queries are the last
+    N_q positions of the sequence: query i sits at position i + N_k - N_q, and
+    the causal mask and the window are taken between positions (bottom-right
+    alignment), so query N_q - 1 sees every key;
   * LSE is the natural log over the *scaled* scores, masked keys excluded;
   * head h of the query reads K/V head floor(h / G), G = H_q / H_kv
     (contiguous groups);
@@ -92,16 +97,17 @@ def to_f64(x) -> torch.Tensor:
     return t.to(device="cpu", dtype=torch.float64).contiguous()
 
 
-def _shapes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool):
-    """(B, H_q, H_kv, N_q, d, G).  Keys may number N_k != N_q only without a mask."""
+def _shapes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, positional: bool):
+    """(B, H_q, H_kv, N_q, d, G).  With a positional mask (causal or window) the
+    queries are the last N_q of N_k >= N_q positions; without one any N_k."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, Hq, N, d = q.shape
     Bk, Hkv, Nk, dk = k.shape
     if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
-    if causal and Nk != N:
-        raise ValueError("the causal mask needs as many keys as queries")
+    if positional and Nk < N:
+        raise ValueError("a causal or windowed mask needs at least as many keys as queries")
     if Hkv <= 0 or Hq % Hkv != 0:
         raise ValueError("H_q must be a multiple of H_kv")
     return B, Hq, Hkv, N, d, Hq // Hkv
@@ -117,7 +123,7 @@ def _row_probs(q_rows: torch.Tensor, k_head: torch.Tensor, rows: torch.Tensor,
                window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Scores -> (P, LSE) for a set of query rows of one head, over all keys.
 
-    q_rows [R, d], k_head [N, d], rows [R] = the query positions i of q_rows.
+    q_rows [R, d], k_head [N, d], rows [R] = the sequence positions of q_rows.
     Returns P [R, N] (exact zeros where masked) and LSE [R].
     """
     N = k_head.shape[0]
@@ -141,7 +147,7 @@ def attention_forward(q, k, v, causal: bool, scale: Optional[float] = None,
     """O [B,H_q,N,d] and LSE [B,H_q,N], both float64."""
     _check_window(window)
     q, k, v = to_f64(q), to_f64(k), to_f64(v)
-    B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal)
+    B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal or window is not None)
     tau = default_scale(d) if scale is None else float(scale)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float64)
@@ -150,7 +156,7 @@ def attention_forward(q, k, v, causal: bool, scale: Optional[float] = None,
             g = h // G
             for r0 in range(0, N, row_block):
                 r1 = min(N, r0 + row_block)
-                rows = torch.arange(r0, r1, dtype=torch.int64)
+                rows = torch.arange(r0, r1, dtype=torch.int64) + (k.shape[2] - N)   # positions
                 p, l_blk = _row_probs(q[b, h, r0:r1], k[b, g], rows, causal, tau, window)
                 o[b, h, r0:r1] = p @ v[b, g]
                 lse[b, h, r0:r1] = l_blk
@@ -162,10 +168,10 @@ def attention_probs(q, k, causal: bool, scale: Optional[float] = None,
     """The full probability matrix P [B,H_q,N_q,N_k] (small inputs only)."""
     _check_window(window)
     q, k = to_f64(q), to_f64(k)
-    B, Hq, Hkv, N, d, G = _shapes(q, k, k, causal)
+    B, Hq, Hkv, N, d, G = _shapes(q, k, k, causal or window is not None)
     tau = default_scale(d) if scale is None else float(scale)
     out = torch.empty((B, Hq, N, k.shape[2]), dtype=torch.float64)
-    rows = torch.arange(N, dtype=torch.int64)
+    rows = torch.arange(N, dtype=torch.int64) + (k.shape[2] - N)               # positions
     for b in range(B):
         for h in range(Hq):
             out[b, h], _ = _row_probs(q[b, h], k[b, h // G], rows, causal, tau, window)
@@ -188,7 +194,7 @@ def forward_rows(q, k, v, causal: bool, scale: Optional[float], b: int, h: int,
     _check_window(window)
     q_r = to_f64(q[b, h])[rows_t]
     k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
-    p, lse = _row_probs(q_r, k_g, rows_t, causal, tau, window)
+    p, lse = _row_probs(q_r, k_g, rows_t + (k.shape[2] - q.shape[2]), causal, tau, window)
     return p @ v_g, lse
 
 
@@ -197,7 +203,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,
     """dQ [B,H_q,N,d], dK and dV [B,H_kv,N,d] of L = sum(dO * O), float64."""
     _check_window(window)
     q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
-    B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal)
+    B, Hq, Hkv, N, d, G = _shapes(q, k, v, causal or window is not None)
     if tuple(do.shape) != tuple(q.shape):
         raise ValueError("dO must have the shape of Q")
     tau = default_scale(d) if scale is None else float(scale)
@@ -209,7 +215,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,
             g = h // G
             for r0 in range(0, N, row_block):
                 r1 = min(N, r0 + row_block)
-                rows = torch.arange(r0, r1, dtype=torch.int64)
+                rows = torch.arange(r0, r1, dtype=torch.int64) + (k.shape[2] - N)   # positions
                 q_blk, do_blk = q[b, h, r0:r1], do[b, h, r0:r1]
                 p, _ = _row_probs(q_blk, k[b, g], rows, causal, tau, window)
                 dp = do_blk @ v[b, g].transpose(0, 1)          # dP_ij = dO_i . v_j
@@ -237,7 +243,7 @@ def backward_dq_rows(q, k, v, do, causal: bool, scale: Optional[float], b: int,
     q_r = to_f64(q[b, h])[rows_t]
     do_r = to_f64(do[b, h])[rows_t]
     k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
-    p, _ = _row_probs(q_r, k_g, rows_t, causal, tau, window)
+    p, _ = _row_probs(q_r, k_g, rows_t + (k.shape[2] - q.shape[2]), causal, tau, window)
     dp = do_r @ v_g.transpose(0, 1)
     c = (p * dp).sum(dim=1)
     ds = p * (dp - c[:, None])

@@ -11,8 +11,9 @@ It follows the same definitions, from the pages named in
 ([EVOL] §2, "从“算力黑洞”到“效率革命”：大模型Attention的演进之路"), causal keys
 j <= i ([EVOL] §6), K/V head floor(h/G) for grouped queries ([EVOL] §3), the
 natural-log log-sum-exp statistic ([LONGCTX] §2.2, cccbook ch. 6.1), the
-sliding window of w keys on each side of a query ([LONGCTX] §4), and the
-analytic softmax gradients.  Only use it for N * N * d up to ~10^5.
+sliding window of w keys on each side of a query ([LONGCTX] §4), queries that
+are the last N_q of N_k positions when decoding against a KV cache ([EVOL] §1,
+§3; [LONGCTX] §1.5), and the analytic softmax gradients (N_q = N_k only).  Only use it for N * N * d up to ~10^5.
 """
 from __future__ import annotations
 
@@ -29,13 +30,15 @@ def tolist4(x) -> List:
     return [[[[float(e) for e in row] for row in head] for head in bat] for bat in x]
 
 
-def _visible(i: int, n: int, causal: bool, window=None) -> List[int]:
-    """Key positions query i attends to, in increasing order."""
+def _visible(i: int, n: int, causal: bool, window=None, nq=None) -> List[int]:
+    """Keys (of n) that query i (of nq, default n) attends to, in increasing
+    order.  With nq < n the queries are the last nq positions of the sequence."""
+    pos = i + n - (n if nq is None else nq)
     out = []
     for j in range(n):
-        if causal and j > i:
+        if causal and j > pos:
             continue
-        if window is not None and abs(i - j) > window:
+        if window is not None and abs(pos - j) > window:
             continue
         out.append(j)
     return out
@@ -49,7 +52,7 @@ def bf_forward(q, k, v, causal: bool, scale: float, window=None):
     """Returns (O, LSE) as nested lists: O[b][h][i][t], LSE[b][h][i]."""
     q, k, v = tolist4(q), tolist4(k), tolist4(v)
     B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
-    Hkv = len(k[0])
+    Hkv, Nk = len(k[0]), len(k[0][0])
     G = Hq // Hkv
     O = [[[[0.0] * d for _ in range(N)] for _ in range(Hq)] for _ in range(B)]
     L = [[[0.0] * N for _ in range(Hq)] for _ in range(B)]
@@ -57,7 +60,7 @@ def bf_forward(q, k, v, causal: bool, scale: float, window=None):
         for h in range(Hq):
             g = h // G
             for i in range(N):
-                keys = _visible(i, N, causal, window)
+                keys = _visible(i, Nk, causal, window, N)
                 s = [scale * _dot(q[b][h][i], k[b][g][j]) for j in keys]
                 m = max(s)
                 lse = m + math.log(math.fsum(math.exp(x - m) for x in s))

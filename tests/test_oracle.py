@@ -405,3 +405,47 @@ def test_negative_window_is_rejected():
     q = rnd(61, 1, 1, 4, 4)
     with pytest.raises(ValueError):
         attention_forward(q, q, q, True, window=-1)
+
+
+# --------------------------------------------------------------------------
+# decoding against a KV cache: N_q < N_k, queries are the last N_q positions
+# ([EVOL] §1 and §3, [LONGCTX] §1.5)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("nq", [1, 2, 5, 13])
+def test_decode_matches_bruteforce(nq, causal):
+    B, Hq, Hkv, Nk, d = 2, 4, 2, 13, 8
+    q, k, v = rnd(70, B, Hq, nq, d), rnd(71, B, Hkv, Nk, d), rnd(72, B, Hkv, Nk, d)
+    o, lse = attention_forward(q, k, v, causal, 0.43, row_block=2)
+    bo, bl = bf_forward(q, k, v, causal, 0.43)
+    assert max_rel(o, bo) < 1e-12 and max_rel(lse, bl) < 1e-12
+
+
+@pytest.mark.parametrize("window", [None, 3])
+def test_decode_is_the_tail_of_the_full_problem(window):
+    """Bottom-right alignment: the last N_q rows of the full causal problem are
+    exactly the decode of those N_q queries against all N_k keys."""
+    B, Hq, Hkv, Nk, d = 1, 4, 1, 40, 8
+    q, k, v = rnd(73, B, Hq, Nk, d), rnd(74, B, Hkv, Nk, d), rnd(75, B, Hkv, Nk, d)
+    o, lse = attention_forward(q, k, v, True, window=window)
+    for nq in (1, 3, 17):
+        od, ld = attention_forward(q[:, :, -nq:], k, v, True, window=window)
+        assert torch.allclose(od, o[:, :, -nq:], atol=1e-14) and torch.allclose(ld, lse[:, :, -nq:], atol=1e-14)
+        ro, rl = forward_rows(q[:, :, -nq:], k, v, True, None, 0, 2, [0, nq - 1], window=window)
+        assert torch.allclose(ro, o[0, 2, [Nk - nq, Nk - 1]], atol=1e-14)
+
+
+def test_decode_single_query_sees_every_key():
+    """N_q = 1, causal: the one query sits at the last position, so the mask
+    hides nothing and the result equals the unmasked one."""
+    q, k, v = rnd(76, 1, 2, 1, 8), rnd(77, 1, 2, 30, 8), rnd(78, 1, 2, 30, 8)
+    o1, l1 = attention_forward(q, k, v, True)
+    o0, l0 = attention_forward(q, k, v, False)
+    assert torch.equal(o1, o0) and torch.equal(l1, l0)
+
+
+def test_positional_mask_needs_enough_keys():
+    q, k = rnd(79, 1, 1, 5, 4), rnd(80, 1, 1, 4, 4)
+    with pytest.raises(ValueError):
+        attention_forward(q, k, k, True)
+    attention_forward(q, k, k, False)           # no mask: any number of keys

@@ -25,8 +25,10 @@ MUTANTS = {
     "mask_hides_diagonal": ("keys[None, :] > rows[:, None]", "keys[None, :] >= rows[:, None]"),
     "mask_shows_next_key": ("keys[None, :] > rows[:, None]", "keys[None, :] > rows[:, None] + 1"),
     "lse_drops_max": ("lse = m + torch.log(ell)", "lse = torch.log(ell)"),
-    "gqa_modulo_heads": ("            g = h // G\n            for r0 in range(0, N, row_block):\n                r1 = min(N, r0 + row_block)\n                rows = torch.arange(r0, r1, dtype=torch.int64)\n                p, l_blk",
-                         "            g = h % Hkv\n            for r0 in range(0, N, row_block):\n                r1 = min(N, r0 + row_block)\n                rows = torch.arange(r0, r1, dtype=torch.int64)\n                p, l_blk"),
+    "gqa_modulo_heads": ("            g = h // G\n            for r0 in range(0, N, row_block):\n                r1 = min(N, r0 + row_block)\n                rows = torch.arange(r0, r1, dtype=torch.int64) + (k.shape[2] - N)   # positions\n                p, l_blk",
+                         "            g = h % Hkv\n            for r0 in range(0, N, row_block):\n                r1 = min(N, r0 + row_block)\n                rows = torch.arange(r0, r1, dtype=torch.int64) + (k.shape[2] - N)   # positions\n                p, l_blk"),
+    "decode_top_left_alignment": ("rows = torch.arange(r0, r1, dtype=torch.int64) + (k.shape[2] - N)   # positions\n                p, l_blk",
+                                  "rows = torch.arange(r0, r1, dtype=torch.int64)\n                p, l_blk"),
     "jacobian_sign": ("ds = p * (dp - c[:, None])                     # dS_ij", "ds = p * (dp + c[:, None])                     # dS_ij"),
     "jacobian_drops_c": ("ds = p * (dp - c[:, None])                     # dS_ij", "ds = p * dp                     # dS_ij"),
     "dk_no_scale": ("dk[b, g] += tau * (ds.transpose(0, 1) @ q_blk)", "dk[b, g] += (ds.transpose(0, 1) @ q_blk)"),
@@ -77,6 +79,12 @@ def pins_pass(mod) -> bool:
             for x, y in zip(g, bg):
                 if not torch.allclose(x, torch.tensor(y, dtype=torch.float64), atol=1e-10):
                     return False
+            qd = q[:, :, -3:]                       # decode: the last 3 queries against 9 keys
+            o, lse = mod.attention_forward(qd, k, v, causal, 0.37, row_block=2)
+            bo, bl = bf_forward(qd, k, v, causal, 0.37)
+            if not (torch.allclose(o, torch.tensor(bo, dtype=torch.float64), atol=1e-11)
+                    and torch.allclose(lse, torch.tensor(bl, dtype=torch.float64), atol=1e-11)):
+                return False
             for w in (0, 2):
                 o, lse = mod.attention_forward(q, k, v, causal, 0.37, row_block=4, window=w)
                 bo, bl = bf_forward(q, k, v, causal, 0.37, window=w)
