@@ -34,7 +34,8 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s (causal bf16, d=128) at N=8K–32K; % of MFMA bf16 peak"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
-BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K")
+BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K", "decode-32K")
+PEAK_HBM_GBPS = 8000.0
 
 
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
@@ -47,6 +48,7 @@ KERNEL_SOURCES = {
     "bwd_dkdv_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
     "bwd_dq_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
     "bwd_grads_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
+    "attn_decode_split_kernel": ("attn_device.h", "attn_layout.h", "attn_decode.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -153,12 +155,13 @@ def cpu_baseline(w, x, n_heads):
 
     hq = max(1, min(n_heads, w.Hq))
     hk = max(1, hq // w.group)            # the K/V heads those query heads read
-    sl = lambda name, h: torch.from_numpy(bf16_bits_to_f64(x[name][:1, :h].copy()))
+    nb = w.B if w.nq is not None else 1   # decoding is cheap enough to take every sequence
+    sl = lambda name, h: torch.from_numpy(bf16_bits_to_f64(x[name][:nb, :h].copy()))
     q, k, v = sl("q", hq), sl("k", hk), sl("v", hk)
     threads = torch.get_num_threads()
     t0 = time.perf_counter()
     attention_forward(q, k, v, True, window=w.window)
-    pairs = hq * w.keys_per_query(True)
+    pairs = nb * hq * w.keys_per_query(True)
     flops = 4 * w.d * pairs
     if w.with_grad:
         attention_backward(q, k, v, sl("do", hq), True, window=w.window)
@@ -170,7 +173,7 @@ def cpu_baseline(w, x, n_heads):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fp64 oracle {what} on batch 0, query heads 0..{hq - 1} of {w.Hq}, full N={w.N}, "
+        "sample": f"fp64 oracle {what} on batches 0..{nb - 1}, query heads 0..{hq - 1} of {w.Hq}, full N={w.N}, "
                   f"same seeded inputs (algorithmic {flops:.3g} FLOP in {dt:.2f} s; the oracle "
                   f"evaluates full masked rows)",
         "host": platform.processor() or platform.machine(),
@@ -215,24 +218,33 @@ def main():
 
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    nq = w.N if w.nq is None else w.nq
+    lse = torch.empty((w.B, w.Hq, nq), dtype=torch.float32, device="cuda")
+    decode = w.nq is not None
+    if decode:
+        ws = torch.empty(attn.decode_workspace_bytes(w.B, w.Hq, w.Hkv, nq, w.N, w.d), dtype=torch.uint8,
+                         device="cuda")
     if w.with_grad:
         do = dev(x["do"])
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         delta = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    # Each phase is one kernel launch; events between them give per-kernel
-    # durations on the stream the kernels run on.  The two backward phases are
-    # exactly what attn_bwd runs, in the same order.
-    phases = ["fwd"] + (["bwd_pre", "bwd_grads"] if w.with_grad else [])
+    # Each phase is one kernel launch (the decode phase: the split kernel and
+    # its small merge); events between them give per-kernel durations on the
+    # stream the kernels run on.  The two backward phases are exactly what
+    # attn_bwd runs, in the same order.
+    phases = (["decode"] if decode else ["fwd"]) + (["bwd_pre", "bwd_grads"] if w.with_grad else [])
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream, window=w.window)
+        if decode:
+            attn.fwd_decode(q, k, v, causal=True, out=o, lse=lse, workspace=ws, stream=stream)
+        else:
+            attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream, window=w.window)
         mark(1)
         if w.with_grad:
             attn.bwd_preprocess(o, do, delta, stream=stream)
@@ -268,9 +280,9 @@ def main():
     # and PV (4d); the gradient kernel's S, dP, dV, dK and dQ (10d -- the dQ
     # blocks' second S and dP are recomputation and not counted); the pre-pass
     # does no matmul.
-    per_pair = {"fwd": 4 * w.d, "bwd_pre": 0, "bwd_grads": 10 * w.d}
+    per_pair = {"fwd": 4 * w.d, "bwd_pre": 0, "bwd_grads": 10 * w.d, "decode": 4 * w.d}
     kernel_name = {"fwd": "attn_fwd_kernel", "bwd_pre": "bwd_pre_kernel",
-                   "bwd_grads": "bwd_grads_kernel"}
+                   "bwd_grads": "bwd_grads_kernel", "decode": "attn_decode_split_kernel"}
     fwd_flops = w.fwd_flops(True)
     bwd_flops = w.bwd_flops(True) if w.with_grad else 0
     step_flops = fwd_flops + bwd_flops
@@ -290,11 +302,22 @@ def main():
                               "pct_of_peak": 100 * bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
 
     dom = max(phases, key=lambda p: parts[p]["ms_avg"])
-    achieved = parts[dom]["tflops"]
     traffic = recorded_traffic(kernel_name[dom], w.name)
-    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel_name[dom],
-                "ms_per_launch": parts[dom]["ms_avg"], "algorithmic_flops_per_launch": parts[dom]["algorithmic_flops"]}
+    if decode:
+        # HBM-bound: K and V once, Q in, O and LSE out
+        alg_bytes = 2 * w.B * w.Hkv * w.N * w.d * 2 + 2 * w.B * w.Hq * nq * w.d * 2 + w.B * w.Hq * nq * 4
+        gbps = alg_bytes / (parts[dom]["ms_avg"] * 1e-3) / 1e9
+        parts[dom]["algorithmic_bytes"] = alg_bytes
+        parts[dom]["gbps"] = gbps
+        roofline = {"bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": gbps / PEAK_HBM_GBPS, "traffic": traffic, "kernel": kernel_name[dom],
+                    "ms_per_launch": parts[dom]["ms_avg"], "algorithmic_bytes_per_launch": alg_bytes}
+    else:
+        achieved = parts[dom]["tflops"]
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel_name[dom],
+                    "ms_per_launch": parts[dom]["ms_avg"],
+                    "algorithmic_flops_per_launch": parts[dom]["algorithmic_flops"]}
 
     result = {
         "metric": METRIC,
@@ -310,15 +333,16 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": True, "pass": "fwd+bwd" if w.with_grad else "fwd",
+                   "causal": True, "pass": "fwd+bwd" if w.with_grad else ("decode" if decode else "fwd"),
                    "flops_per_step": step_flops, "seed": w.seed, "input_scale": w.in_scale,
-                   "window": w.window},
+                   "window": w.window, "queries": nq},
         "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
         "parts": parts,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1}[w.name]
+        default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1,
+                         "decode-32K": 32}[w.name]
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_heads or default_heads)
     print(json.dumps(result), flush=True)
 

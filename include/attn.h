@@ -166,6 +166,35 @@ int attn_bwd_grads_window(const void* q, const void* k, const void* v, const voi
                           int B, int Hq, int Hkv, int N, int d, int causal, int window,
                           float scale, void* stream);
 
+/*
+ * Forward for decoding against a KV cache (pages "从“算力黑洞”到“效率革命”：
+ * 大模型Attention的演进之路", §1 and §3, and "6.1 … 長上下文擴展技術", §1.5): a
+ * few new queries attend to a long cached K/V history.  The Nq queries are the
+ * last Nq positions of a sequence of Nk (query i at position i + Nk - Nq); the
+ * causal mask and the window are taken between positions, so with causal the
+ * last query sees every key.  The key axis is split into chunks processed in
+ * parallel, and the per-chunk (O, LSE) partials are merged by their
+ * log-sum-exp (page "6.1 …", §2.2: the online softmax makes that exact).
+ *
+ *   q      [B, Hq,  Nq, d] bf16, read;  o [B, Hq, Nq, d] bf16, written
+ *   k, v   [B, Hkv, Nk, d] bf16, read (the cache; Nk >= Nq)
+ *   lse    [B, Hq, Nq] fp32, written (natural log of the scaled scores)
+ *   window < 0: none; >= 0: keys with |pos - j| <= window
+ *   num_splits: <= 0 lets the library choose; otherwise an upper bound
+ *     (a chunk is a whole number of 128-key tiles, so fewer may be used)
+ *   workspace: device buffer of workspace_bytes >= the value
+ *     attn_fwd_decode_workspace_bytes returns for the same shapes and
+ *     num_splits; contents on entry ignored, on exit unspecified.
+ * Errors as attn_fwd, with ATTN_ERR_SHAPE also for Nq > Nk and ATTN_ERR_WORKSPACE
+ * for a short workspace.  Deterministic for a fixed num_splits.
+ */
+size_t attn_fwd_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                       int num_splits);
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window,
+                    float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
  * of the last failure on the calling thread.  Never NULL. */
 const char* attn_strerror(int code);

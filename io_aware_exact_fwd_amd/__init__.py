@@ -19,7 +19,8 @@ from typing import Optional, Tuple
 import torch  # loads the HIP runtime that libattn.so then binds to
 
 __all__ = [
-    "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads",
+    "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads", "fwd_decode",
+    "decode_workspace_bytes",
     "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
 ]
@@ -27,7 +28,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads", "attn_strerror",
-            "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window")
+            "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window",
+            "attn_fwd_decode", "attn_fwd_decode_workspace_bytes")
 
 ATTN_OK = 0
 
@@ -69,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_window.restype = i
     L.attn_bwd_grads_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     L.attn_bwd_grads_window.restype = i
+    L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    L.attn_fwd_decode.restype = i
+    L.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_fwd_decode_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_strerror.argtypes = [i]
@@ -272,3 +278,41 @@ def bwd_grads(q, k, v, do, lse, delta, causal: bool = True, scale: Optional[floa
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_bwd_grads" if window is None else "attn_bwd_grads_window")
     return dq, dk, dv
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int,
+                           num_splits: int = 0) -> int:
+    return int(lib().attn_fwd_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, int(num_splits)))
+
+
+def fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+               scale: Optional[float] = None, window: Optional[int] = None, num_splits: int = 0,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode forward: q [B,Hq,Nq,d] against the cache k, v [B,Hkv,Nk,d] (Nq <= Nk,
+    queries at the last Nq positions).  Returns O (bf16) and LSE (fp32 [B,Hq,Nq])."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check_bf16("q", q, (B, Hq, Nq, d))
+    _check_bf16("k", k, (B, Hkv, Nk, d))
+    _check_bf16("v", v, (B, Hkv, Nk, d))
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, (B, Hq, Nq, d))
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_f32("lse", lse, (B, Hq, Nq))
+    need = decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk,
+                               d, int(bool(causal)), -1 if window is None else int(window), tau,
+                               int(num_splits), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_decode")
+    return out, lse
+

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
 HEADERS = ["attn_device.h", "attn_launch.h", "attn_layout.h"]
 
 ARCH = "gfx950"

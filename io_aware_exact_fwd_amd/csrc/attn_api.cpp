@@ -230,6 +230,45 @@ ATTN_EXPORT int attn_bwd_grads_window(const void* q, const void* k, const void* 
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_grads_window launch");
 }
 
+// Shapes of a decode call: Nq queries (the last Nq positions) against Nk keys.
+static int check_decode(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || Nq > Nk) return ATTN_ERR_SHAPE;
+  if ((long long)Nk * d > INT_MAX) return ATTN_ERR_SHAPE;
+  if ((long long)B * Hq * Nq * (d + 1) > INT_MAX) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+ATTN_EXPORT size_t attn_fwd_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                                   int num_splits) {
+  if (check_decode(B, Hq, Hkv, Nq, Nk, d)) return 0;
+  int chunk = 0;
+  const int splits = attn::decode_splits(B, Hq, Hkv, Nq, Nk, num_splits, &chunk);
+  return attn::decode_workspace_bytes(B, Hq, Nq, d, splits);
+}
+
+ATTN_EXPORT int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                                int window, float scale, int num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return ATTN_ERR_NULL;
+  int rc = check_decode(B, Hq, Hkv, Nq, Nk, d);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o, lse, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  int chunk = 0;
+  const int splits = attn::decode_splits(B, Hq, Hkv, Nq, Nk, num_splits, &chunk);
+  if (workspace_bytes < attn::decode_workspace_bytes(B, Hq, Nq, d, splits)) return ATTN_ERR_WORKSPACE;
+  if ((rc = check_scale(scale))) return rc;
+  if ((rc = current_device_check())) return rc;
+  attn::DecodeArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale,
+                     window < 0 ? -1 : window, splits, chunk, (float*)workspace};
+  hipError_t e = attn::launch_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd_decode launch");
+}
+
 ATTN_EXPORT const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";

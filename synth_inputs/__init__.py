@@ -50,10 +50,16 @@ class Workload:
     with_grad: bool = False
     note: str = ""
     window: Optional[int] = None    # sliding window |i - j| <= window, or none
+    nq: Optional[int] = None        # queries, when fewer than the N keys (decoding)
 
     def keys_per_query(self, causal: bool) -> int:
-        """Visible keys summed over the N query rows of one head (a count)."""
+        """Visible keys summed over the query rows of one head (a count)."""
         n, w = self.N, self.window
+        if self.nq is not None:
+            if w is not None:
+                raise ValueError("windowed decode workloads are not defined")
+            m = self.nq      # queries at positions n - m .. n - 1
+            return m * (n - m) + m * (m + 1) // 2 if causal else m * n
         if w is None or w >= n - 1:
             return n * (n + 1) // 2 if causal else n * n
         left = (w + 1) * (w + 2) // 2 + (n - w - 1) * (w + 1)     # keys j in [i - w, i]
@@ -90,6 +96,8 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("fb-32K", 1, 8, 8, 32768, 128, (True,), seed=4, with_grad=True),
         Workload("swa-32K", 1, 8, 8, 32768, 128, (True,), seed=5, with_grad=True, window=4096,
                  note="sliding-window causal attention, 4096 keys back"),
+        Workload("decode-32K", 16, 32, 8, 32768, 128, (True,), seed=6, nq=1,
+                 note="one new query per sequence against a 32768-key cache"),
     )
 }
 
@@ -154,7 +162,13 @@ def make_inputs(workload: str | Workload, seed: Optional[int] = None,
                 keep_f32: bool = False) -> Dict[str, np.ndarray]:
     """Inputs of a named workload (its own seed unless ``seed`` is given)."""
     w = WORKLOADS[workload] if isinstance(workload, str) else workload
-    return make_custom_inputs(w.B, w.Hq, w.Hkv, w.N, w.d,
-                              w.seed if seed is None else seed,
-                              in_scale=w.in_scale, with_grad=w.with_grad,
-                              keep_f32=keep_f32)
+    sd = w.seed if seed is None else seed
+    x = make_custom_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, sd, in_scale=w.in_scale,
+                           with_grad=w.with_grad, keep_f32=keep_f32)
+    if w.nq is not None:
+        # decoding: the N keys are the cache; the queries are a separate draw of nq rows
+        xq = make_custom_inputs(w.B, w.Hq, w.Hkv, w.nq, w.d, sd + 1, in_scale=w.in_scale,
+                                keep_f32=keep_f32)
+        for name in [n for n in xq if n.startswith("q")]:
+            x[name] = xq[name]
+    return x

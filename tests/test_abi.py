@@ -32,7 +32,9 @@ def test_header_declares_the_boundary():
                                            "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
                                            "attn_bwd_grads", "attn_strerror",
                                            "attn_device_check", "attn_fwd_window",
-                                           "attn_bwd_window", "attn_bwd_grads_window"])
+                                           "attn_bwd_window", "attn_bwd_grads_window",
+                                           "attn_fwd_decode",
+                                           "attn_fwd_decode_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -160,4 +162,25 @@ def test_window_entry_points_validate(L):
     assert L.attn_fwd_window(A, A, A, A, A, 1, 2, 2, 16, 64, 1, 4, 0.0, None) == 5
     assert L.attn_bwd_window(A, A, A, A, A, A, A, A, A, A, 0, 1, 2, 2, 16, 64, 1, 4, 0.1, None) == 4
     assert L.attn_bwd_grads_window(*([A] * 8), MIS, 1, 2, 2, 16, 64, 1, 4, 0.1, None) == 3
+
+
+def test_decode_validation_and_workspace(L):
+    """Decode: shape rules (Nq <= Nk), workspace sizing, errors before device work."""
+    ws = L.attn_fwd_decode_workspace_bytes
+    # automatic split count: the workspace holds (d + 1) floats per row per chunk
+    n = ws(2, 8, 2, 1, 4096, 128, 0)
+    assert n > 0 and n % (2 * 8 * 1 * 129 * 4) == 0
+    chunks = n // (2 * 8 * 1 * 129 * 4)
+    assert 1 <= chunks <= 4096 // 128
+    assert ws(1, 4, 4, 3, 1000, 64, 1) == 1 * 4 * 3 * 65 * 4          # one chunk
+    assert ws(1, 4, 4, 3, 1000, 64, 100) == 8 * 4 * 3 * 65 * 4        # at most one chunk per tile
+    assert ws(1, 4, 4, 5, 4, 64, 0) == 0                               # Nq > Nk
+    assert ws(1, 4, 3, 1, 4, 64, 0) == 0                               # Hq % Hkv
+    args = [A] * 5
+    assert L.attn_fwd_decode(*args, 1, 4, 4, 5, 4, 64, 1, -1, 0.1, 0, A, 1 << 20, None) == 2
+    assert L.attn_fwd_decode(*args, 1, 4, 4, 1, 64, 96, 1, -1, 0.1, 0, A, 1 << 20, None) == 3
+    assert L.attn_fwd_decode(*args, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, None, 1 << 20, None) == 1
+    assert L.attn_fwd_decode(*args, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, A, 16, None) == 4
+    assert L.attn_fwd_decode(*args, 1, 4, 4, 1, 64, 64, 1, -1, -1.0, 0, A, 1 << 20, None) == 5
+    assert L.attn_fwd_decode(A, A, MIS, A, A, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, A, 1 << 20, None) == 3
 
