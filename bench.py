@@ -80,7 +80,8 @@ def _per_kernel(csv_path: str, counter: str):
 
 def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str,
                     mfma_csv: str | None = None) -> dict:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> profiles/counters.json.
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) -> the workload's record in
+    profiles/counters.json (records of other workloads are kept).
 
     Both counters are scaled by what they read for the plain copy of calib_mib
     MiB that ran in the same process (it reads and writes calib_mib MiB).
@@ -108,8 +109,14 @@ def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: st
             e["grbm_gui_active"] = mfma["GRBM_GUI_ACTIVE"][k]
         out["kernels"][k] = e
     os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
+    try:
+        with open(COUNTERS_JSON) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = out
     with open(COUNTERS_JSON, "w") as fh:
-        json.dump(out, fh, indent=1)
+        json.dump(allrec, fh, indent=1)
     return out
 
 
@@ -118,11 +125,11 @@ def recorded_traffic(kernel: str, workload: str):
     sources changed since they were taken (or none were taken)."""
     try:
         with open(COUNTERS_JSON) as fh:
-            rec = json.load(fh)
+            rec = json.load(fh).get(workload, {})
     except (OSError, ValueError):
         return None
     e = rec.get("kernels", {}).get(kernel)
-    if rec.get("workload") != workload or not e or e.get("source_sha") != source_sha(kernel):
+    if not e or e.get("source_sha") != source_sha(kernel):
         return None
     return e["hbm_bytes"]
 

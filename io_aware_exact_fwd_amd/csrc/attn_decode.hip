@@ -23,7 +23,13 @@
 //     O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 with the same tile layout,
 //     direct loads and fragment reads as the main forward; each wave keeps its
 //     own running max, sum and accumulator;
-//   * at the end the four waves' partials meet in LDS and are merged, and the
+//   * the tiles stream through an LDS ring of up to 128 KB (two 64 KB stages
+//     for d = 128, four 32 KB stages for d = 64): the next tiles' loads are in
+//     flight while one tile is computed, and each wave waits only for the
+//     oldest (vmcnt counts the newer tiles' loads).  Measured on d = 128:
+//     deeper rings of smaller tiles, or two workgroups per CU, read no faster;
+//     the kernel streams K and V at the rate a plain read kernel reaches;
+//   * at the end the waves' partials meet in LDS and are merged, and the
 //     chunk's normalised O (fp32) and LSE are written to the workspace;
 //   * a second kernel merges the chunks of every row into O (bf16) and LSE.
 #include "attn_device.h"
@@ -32,19 +38,44 @@
 namespace attn {
 namespace {
 
-constexpr int kDecBC = 128;   // keys per tile
-constexpr int kDecNW = 4;     // waves per workgroup, 32 keys of each tile each
-constexpr int kDecRows = 32;  // query rows per workgroup
+constexpr int kDecNW = 4;            // waves per workgroup, 32 keys of each tile each
+constexpr int kDecBC = 32 * kDecNW;  // keys per tile
+constexpr int kDecRows = 32;         // query rows per workgroup
+constexpr int kDecLdsBudget = 128 * 1024;
+constexpr int kDecMaxStages = 4;
 
 template <int D>
 struct DecCfg {
   static constexpr int kTile = kDecBC * 2 * D;      // bytes of one K or V tile
-  static constexpr int kLdsBytes = 2 * 2 * kTile;   // double-buffered K and V
+  // tiles resident in the LDS ring
+  static constexpr int kStages = kDecLdsBudget / (2 * kTile) < kDecMaxStages
+                                     ? kDecLdsBudget / (2 * kTile) : kDecMaxStages;
+  static constexpr int kLdsBytes = kStages * 2 * kTile;
+  // direct loads one wave issues per tile (K and V)
+  static constexpr int kLoadsPerTile = 2 * TileLoader<D, kDecBC, kDecNW>::kPer;
+  static_assert(kStages >= 2, "at least double buffering");
+  static_assert(TileLoader<D, kDecBC, kDecNW>::kSegs % kDecNW == 0, "every wave issues kPer loads");
+  static_assert((kStages - 2) * kLoadsPerTile < 64, "vmcnt range");
   // the merge reuses the tile memory: per wave m and l (32 rows each) and the
   // O^T accumulator (D x 32 fp32)
   static constexpr int kMergeBytes = kDecNW * (2 * kDecRows + D * kDecRows) * 4;
   static_assert(kMergeBytes <= kLdsBytes, "merge fits in the tile memory");
 };
+
+// Barrier once this wave has at most `later` tiles' loads outstanding
+// (PER loads per tile, later <= MAXL).
+template <int PER, int MAXL>
+__device__ __forceinline__ void barrier_tiles_at_most(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      barrier_vmem_at_most<MAXL * PER>();
+      return;
+    }
+    barrier_tiles_at_most<PER, MAXL - 1>(later);
+  } else {
+    barrier_vmem_at_most<0>();
+  }
+}
 
 // Workspace layout: o_part [splits][B*Hq*Nq][D] fp32, then lse_part
 // [splits][B*Hq*Nq] fp32.
@@ -89,6 +120,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDecNW * 64, kDecNW * 64),
 #pragma unroll
   for (int sl = 0; sl < DS; ++sl)
     qf[sl] = row_ok ? *(const u32x4*)(Q + row_id * D + sl * 16 + 8 * hi) : zero4();
+  // Take the Q loads' wait here, once: left to the compiler it lands at the
+  // first MFMA inside the key loop as a full vmcnt(0), which would also drain
+  // the K/V tiles in flight on every iteration.
+#pragma unroll
+  for (int sl = 0; sl < DS; ++sl) asm volatile("" ::"v"(qf[sl]));
 
   // key range of the chunk, narrowed with a window to what the earliest query
   // (position N_k - N_q) can see
@@ -100,8 +136,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDecNW * 64, kDecNW * 64),
 
   TileLoader<D, kDecBC, kDecNW> ldr;
   ldr.init(wave, lane);
-  auto issue_tile = [&](int j, int buf) {
-    unsigned char* kt = smem + buf * 2 * C::kTile;
+  auto stage = [&](int j) { return smem + (j % C::kStages) * 2 * C::kTile; };
+  auto issue_tile = [&](int j) {
+    unsigned char* kt = stage(j);
     ldr.load(Kp, j * kDecBC, Nk, kt, wave);
     ldr.load(Vp, j * kDecBC, Nk, kt + C::kTile, wave);
   };
@@ -111,17 +148,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDecNW * 64, kDecNW * 64),
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (j_first < n_tiles) {
-    issue_tile(j_first, j_first & 1);
-    wait_all_memory();
-    __syncthreads();
-  }
+  for (int j = j_first; j < min(n_tiles, j_first + C::kStages - 1); ++j) issue_tile(j);
   for (int j = j_first; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
+    // tile j has landed once at most the loads of the tiles issued after it
+    // are outstanding; the barrier then also orders the last reads of stage
+    // (j - 1) before its reuse by tile j + kStages - 1
+    barrier_tiles_at_most<C::kLoadsPerTile, C::kStages - 2>(min(n_tiles - 1 - j, C::kStages - 2));
+    if (j + C::kStages - 1 < n_tiles) issue_tile(j + C::kStages - 1);
     const int kw = j * kDecBC + wave * 32;         // this wave's 32 keys
     if (kw < k_end && kw + 31 >= k_begin) {
-      const unsigned char* kt = smem + buf * 2 * C::kTile;
+      const unsigned char* kt = stage(j);
       const unsigned char* vt = kt + C::kTile;
       f32x16 s = f32x16{};
 #pragma unroll
@@ -164,11 +200,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDecNW * 64, kDecNW * 64),
         acc[db] = mfma_32x32x16(tr_frag<D>(vt, lane, wave * 32 + 16, db * 32), pb1, acc[db]);
       }
     }
-    wait_all_memory();
-    __syncthreads();
   }
+  wait_all_memory();
+  __syncthreads();
 
-  // ---- merge the four waves' partials in LDS ----
+  // ---- merge the waves' partials in LDS ----
   const float l_tot = pair_sum(l_run);
   float* m_l = (float*)smem;                        // [wave][32] running max (log2 units)
   float* l_l = m_l + kDecNW * kDecRows;             // [wave][32] sums
@@ -183,7 +219,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kDecNW * 64, kDecNW * 64),
     for (int i = 0; i < 16; ++i) a_l[((wave * DB + db) * 16 + i) * 64 + lane] = acc[db][i];
   __syncthreads();
 
-  // wave w combines d block w (and w + 4 when D has more blocks than waves)
+  // wave w combines d blocks w, w + kDecNW, ...
   float M = -INFINITY;
 #pragma unroll
   for (int v = 0; v < kDecNW; ++v) M = fmaxf(M, m_l[v * kDecRows + l32]);

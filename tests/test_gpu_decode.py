@@ -6,7 +6,8 @@ reading in the oracle).  Bars as for the forward: max |O| error <= 1e-2, max
 |LSE| error <= 1e-3.  Cases cover one and several query rows per K/V head
 group (G * N_q of 1, 8, 32, 40 rows: one and two 32-row blocks), ragged cache
 lengths, one chunk, many chunks, chunks ending mid-way through the causal
-diagonal, windows, d = 64 and 128, and N_q = N_k.
+diagonal, windows, d = 64 and 128 (each with chunks long enough to cycle the
+LDS ring), and N_q = N_k.
 """
 import pytest
 import torch
@@ -49,6 +50,8 @@ CASES = [
     (1, 8, 2, 2, 3000, 128, 500, 0),
     (1, 4, 1, 16, 1200, 64, 100, 4),
     (1, 4, 2, 300, 300, 128, None, 0),      # N_q = N_k
+    (1, 8, 2, 1, 5000, 64, None, 1),        # d = 64: one 40-tile chunk through the 4-stage ring
+    (1, 8, 8, 3, 6000, 64, 2500, 2),        # d = 64 ring with a long window
 ]
 
 
