@@ -9,10 +9,12 @@ executes this code, and this code never imports the library.
 ``oracle.bruteforce`` -- scalar pure-Python loops that pin the above.
 """
 from .attention import (attention_backward, attention_forward, attention_probs,
-                        backward_dq_rows, default_scale, forward_rows, to_f64)
+                        backward_dq_rows, check_cu_seqlens, default_scale, forward_rows, to_f64,
+                        varlen_backward, varlen_forward, varlen_forward_rows)
 from .bruteforce import bf_backward, bf_forward
 
 __all__ = [
     "attention_forward", "attention_backward", "attention_probs", "forward_rows",
     "backward_dq_rows", "default_scale", "to_f64", "bf_forward", "bf_backward",
+    "varlen_forward", "varlen_backward", "varlen_forward_rows", "check_cu_seqlens",
 ]

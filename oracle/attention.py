@@ -59,7 +59,15 @@ Readings where the pages leave a step open:
     (contiguous groups);
   * the backward is the analytic derivative of the forward (the pages print no
     gradient formulas) and uses the textbook c_i, not the rowsum(dO * O)
-    shortcut a fast kernel may take.
+    shortcut a fast kernel may take;
+  * packed variable-length batches ([EVOL] §6, scenario 2: long-context
+    training data is built by concatenating and packing documents into long
+    sequences): each packed sequence is its own attention problem -- its
+    queries see only its own keys, positions counted from its first token --
+    so a packed batch is the definition above applied to every sequence on
+    its own.  Layout [H, T, d]: sequence b is rows cu_seqlens[b] ..
+    cu_seqlens[b+1] - 1 of every head (cu_seqlens[0] = 0, non-decreasing,
+    cu_seqlens[B] = T; empty sequences allowed); LSE is [H_q, T].
 
 Query rows are processed in blocks only to bound memory (a full 32K x 32K
 fp64 score matrix is 8 GiB); every row is materialised over all N keys with
@@ -80,6 +88,10 @@ __all__ = [
     "attention_probs",
     "forward_rows",
     "backward_dq_rows",
+    "varlen_forward",
+    "varlen_backward",
+    "varlen_forward_rows",
+    "check_cu_seqlens",
     "to_f64",
 ]
 
@@ -248,3 +260,76 @@ def backward_dq_rows(q, k, v, do, causal: bool, scale: Optional[float], b: int,
     c = (p * dp).sum(dim=1)
     ds = p * (dp - c[:, None])
     return tau * (ds @ k_g)
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches: every sequence on its own
+# ---------------------------------------------------------------------------
+def check_cu_seqlens(cu_seqlens, total: int) -> list:
+    """Sequence boundaries as a list of ints; raises unless they start at 0,
+    never decrease and end at the packed length ``total``."""
+    cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    if len(cu) < 2 or cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError(f"cu_seqlens must rise from 0 to {total}: {cu}")
+    return cu
+
+
+def _packed_shapes(q, k, v):
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("packed tensors are [H, T, d]")
+    if k.shape[1] != q.shape[1] or k.shape[2] != q.shape[2] or q.shape[0] % k.shape[0]:
+        raise ValueError("packed K/V must be [H_kv, T, d] with H_q % H_kv == 0")
+
+
+def varlen_forward(q, k, v, cu_seqlens, causal: bool, scale: Optional[float] = None,
+                   window: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """O [H_q, T, d] and LSE [H_q, T] of a packed batch, float64."""
+    q, k, v = to_f64(q), to_f64(k), to_f64(v)
+    _packed_shapes(q, k, v)
+    cu = check_cu_seqlens(cu_seqlens, q.shape[1])
+    if scale is None:
+        scale = default_scale(q.shape[2])
+    o = torch.zeros_like(q)
+    lse = torch.zeros(q.shape[:2], dtype=torch.float64)
+    for s0, s1 in zip(cu, cu[1:]):
+        if s1 == s0:
+            continue
+        ob, lb = attention_forward(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1],
+                                   causal, scale, window=window)
+        o[:, s0:s1] = ob[0]
+        lse[:, s0:s1] = lb[0]
+    return o, lse
+
+
+def varlen_backward(q, k, v, do, cu_seqlens, causal: bool, scale: Optional[float] = None,
+                    window: Optional[int] = None):
+    """dQ [H_q, T, d], dK and dV [H_kv, T, d] of L = sum(dO * O) over a packed batch."""
+    q, k, v, do = to_f64(q), to_f64(k), to_f64(v), to_f64(do)
+    _packed_shapes(q, k, v)
+    cu = check_cu_seqlens(cu_seqlens, q.shape[1])
+    if scale is None:
+        scale = default_scale(q.shape[2])
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    for s0, s1 in zip(cu, cu[1:]):
+        if s1 == s0:
+            continue
+        g = attention_backward(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1],
+                               do[None, :, s0:s1], causal, scale, window=window)
+        dq[:, s0:s1], dk[:, s0:s1], dv[:, s0:s1] = g[0][0], g[1][0], g[2][0]
+    return dq, dk, dv
+
+
+def varlen_forward_rows(q, k, v, cu_seqlens, causal: bool, scale: Optional[float], h: int,
+                        rows: Sequence[int], window: Optional[int] = None):
+    """O and LSE of selected packed rows (global row indices) of query head h,
+    each computed within its own sequence."""
+    cu = check_cu_seqlens(cu_seqlens, q.shape[1])
+    outs, lses = [], []
+    for r in rows:
+        b = max(i for i in range(len(cu) - 1) if cu[i] <= r < cu[i + 1])
+        s0, s1 = cu[b], cu[b + 1]
+        ob, lb = forward_rows(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1], causal,
+                              scale, 0, h, [r - s0], window=window)
+        outs.append(ob[0])
+        lses.append(lb[0])
+    return torch.stack(outs), torch.stack(lses)

@@ -13,7 +13,10 @@ j <= i ([EVOL] §6), K/V head floor(h/G) for grouped queries ([EVOL] §3), the
 natural-log log-sum-exp statistic ([LONGCTX] §2.2, cccbook ch. 6.1), the
 sliding window of w keys on each side of a query ([LONGCTX] §4), queries that
 are the last N_q of N_k positions when decoding against a KV cache ([EVOL] §1,
-§3; [LONGCTX] §1.5), and the analytic softmax gradients (N_q = N_k only).  Only use it for N * N * d up to ~10^5.
+§3; [LONGCTX] §1.5), packed batches whose sequences never see each other
+(``segments``: the sequence id of every position, [EVOL] §6 scenario 2), and
+the analytic softmax gradients (N_q = N_k only).  Only use it for N * N * d up
+to ~10^5.
 """
 from __future__ import annotations
 
@@ -30,15 +33,18 @@ def tolist4(x) -> List:
     return [[[[float(e) for e in row] for row in head] for head in bat] for bat in x]
 
 
-def _visible(i: int, n: int, causal: bool, window=None, nq=None) -> List[int]:
+def _visible(i: int, n: int, causal: bool, window=None, nq=None, segments=None) -> List[int]:
     """Keys (of n) that query i (of nq, default n) attends to, in increasing
-    order.  With nq < n the queries are the last nq positions of the sequence."""
+    order.  With nq < n the queries are the last nq positions of the sequence;
+    with segments, only keys of the query's own segment are seen."""
     pos = i + n - (n if nq is None else nq)
     out = []
     for j in range(n):
         if causal and j > pos:
             continue
         if window is not None and abs(pos - j) > window:
+            continue
+        if segments is not None and segments[j] != segments[pos]:
             continue
         out.append(j)
     return out
@@ -48,7 +54,7 @@ def _dot(a: List[float], b: List[float]) -> float:
     return math.fsum(x * y for x, y in zip(a, b))
 
 
-def bf_forward(q, k, v, causal: bool, scale: float, window=None):
+def bf_forward(q, k, v, causal: bool, scale: float, window=None, segments=None):
     """Returns (O, LSE) as nested lists: O[b][h][i][t], LSE[b][h][i]."""
     q, k, v = tolist4(q), tolist4(k), tolist4(v)
     B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -60,7 +66,7 @@ def bf_forward(q, k, v, causal: bool, scale: float, window=None):
         for h in range(Hq):
             g = h // G
             for i in range(N):
-                keys = _visible(i, Nk, causal, window, N)
+                keys = _visible(i, Nk, causal, window, N, segments)
                 s = [scale * _dot(q[b][h][i], k[b][g][j]) for j in keys]
                 m = max(s)
                 lse = m + math.log(math.fsum(math.exp(x - m) for x in s))
@@ -71,7 +77,7 @@ def bf_forward(q, k, v, causal: bool, scale: float, window=None):
     return O, L
 
 
-def bf_backward(q, k, v, do, causal: bool, scale: float, window=None):
+def bf_backward(q, k, v, do, causal: bool, scale: float, window=None, segments=None):
     """Returns (dQ, dK, dV) as nested lists for L = sum_{b,h,i,t} dO * O."""
     q, k, v, do = tolist4(q), tolist4(k), tolist4(v), tolist4(do)
     B, Hq, N, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
@@ -85,7 +91,7 @@ def bf_backward(q, k, v, do, causal: bool, scale: float, window=None):
         for h in range(Hq):
             g = h // G
             for i in range(N):
-                keys = _visible(i, N, causal, window)
+                keys = _visible(i, N, causal, window, None, segments)
                 s = [scale * _dot(q[b][h][i], k[b][g][j]) for j in keys]
                 m = max(s)
                 lse = m + math.log(math.fsum(math.exp(x - m) for x in s))

@@ -12,13 +12,21 @@ Recipe (per workload, per seed):
   * multiply by the workload's input scale (1.0, or 0.5 -- exact in binary);
   * round fp32 -> bf16 to nearest, ties to even, with integer bit operations.
 
+Packed variable-length batches draw the same way over ``[H, T, d]`` (T the
+packed token count; identical values to the ``[1, H, T, d]`` draw) and add
+``cu_seqlens``; their sequence lengths come from ``pack_lengths``: a
+generator ``PCG64(seed)`` draws ``exp(uniform(ln lo, ln hi))`` rounded to an
+integer, one length at a time, until the pack holds T tokens (the last length
+is cut to fit).
+
 The bf16 payload is returned as ``uint16`` bit patterns; ``bf16_bits_to_f32``
 and ``bf16_bits_to_f64`` decode them exactly.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass, field
-from typing import Dict, Optional, Tuple
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -31,6 +39,8 @@ __all__ = [
     "draw_normal_f32",
     "make_inputs",
     "make_custom_inputs",
+    "pack_lengths",
+    "cu_from_lengths",
 ]
 
 
@@ -51,10 +61,24 @@ class Workload:
     note: str = ""
     window: Optional[int] = None    # sliding window |i - j| <= window, or none
     nq: Optional[int] = None        # queries, when fewer than the N keys (decoding)
+    # packed variable-length batch: N tokens split into sequences whose lengths
+    # are drawn log-uniform in [lo, hi] (pack_lengths with this seed); B = 1
+    pack: Optional[Tuple[int, int]] = None
+
+    def lengths(self) -> List[int]:
+        """Sequence lengths of a packed workload (one sequence of N otherwise)."""
+        if self.pack is None:
+            return [self.N]
+        return pack_lengths(self.N, self.seed, *self.pack)
 
     def keys_per_query(self, causal: bool) -> int:
         """Visible keys summed over the query rows of one head (a count)."""
-        n, w = self.N, self.window
+        if self.pack is not None:
+            return sum(self._keys(n, causal) for n in self.lengths())
+        return self._keys(self.N, causal)
+
+    def _keys(self, n: int, causal: bool) -> int:
+        w = self.window
         if self.nq is not None:
             if w is not None:
                 raise ValueError("windowed decode workloads are not defined")
@@ -98,8 +122,31 @@ WORKLOADS: Dict[str, Workload] = {
                  note="sliding-window causal attention, 4096 keys back"),
         Workload("decode-32K", 16, 32, 8, 32768, 128, (True,), seed=6, nq=1,
                  note="one new query per sequence against a 32768-key cache"),
+        Workload("varlen-32K", 1, 8, 8, 32768, 128, (True,), seed=7, with_grad=True,
+                 pack=(512, 16384),
+                 note="32768 tokens packed from sequences of 512..16384 tokens (log-uniform)"),
     )
 }
+
+
+def pack_lengths(total: int, seed: int, lo: int, hi: int) -> List[int]:
+    """Seeded sequence lengths, log-uniform in [lo, hi], that fill ``total``."""
+    if not (1 <= lo <= hi) or total < 0:
+        raise ValueError("need 1 <= lo <= hi and total >= 0")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out: List[int] = []
+    left = total
+    while left > 0:
+        n = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        n = min(max(n, 1), left)
+        out.append(n)
+        left -= n
+    return out
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    """Sequence boundaries [0, n0, n0 + n1, ...] as int32."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -163,6 +210,13 @@ def make_inputs(workload: str | Workload, seed: Optional[int] = None,
     """Inputs of a named workload (its own seed unless ``seed`` is given)."""
     w = WORKLOADS[workload] if isinstance(workload, str) else workload
     sd = w.seed if seed is None else seed
+    if w.pack is not None:
+        # packed batch: [H, T, d] tensors (the [1, H, T, d] draw) plus the boundaries
+        x = make_custom_inputs(1, w.Hq, w.Hkv, w.N, w.d, sd, in_scale=w.in_scale,
+                               with_grad=w.with_grad, keep_f32=keep_f32)
+        x = {name: a[0] for name, a in x.items()}
+        x["cu_seqlens"] = cu_from_lengths(w.lengths())
+        return x
     x = make_custom_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, sd, in_scale=w.in_scale,
                            with_grad=w.with_grad, keep_f32=keep_f32)
     if w.nq is not None:

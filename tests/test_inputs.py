@@ -71,3 +71,34 @@ def test_flop_counts():
     assert w.fwd_flops(True) == 4 * 128 * w.pairs(True)
     assert abs(w.fwd_flops(True) - 5.498e11) / 5.498e11 < 1e-3
     assert WORKLOADS["fb-32K"].bwd_flops(True) == 10 * 128 * 8 * 32768 * 32769 // 2
+
+
+def test_pack_lengths_fill_the_pack():
+    from synth_inputs import cu_from_lengths, pack_lengths
+    for seed in range(5):
+        L = pack_lengths(32768, seed, 512, 16384)
+        assert sum(L) == 32768 and all(n >= 1 for n in L)
+        assert all(512 <= n <= 16384 for n in L[:-1])    # only the last one is cut
+        assert L == pack_lengths(32768, seed, 512, 16384)
+    assert pack_lengths(0, 1, 1, 4) == []
+    cu = cu_from_lengths([3, 0, 5])
+    assert cu.dtype == np.int32 and cu.tolist() == [0, 3, 3, 8]
+
+
+def test_packed_workload_inputs():
+    from synth_inputs import make_custom_inputs, make_inputs
+    w = WORKLOADS["varlen-32K"]
+    L = w.lengths()
+    assert sum(L) == w.N and w.B == 1
+    assert w.pairs(True) == w.Hq * sum(n * (n + 1) // 2 for n in L)
+    x = make_inputs(w)
+    assert x["q"].shape == (w.Hq, w.N, w.d) and x["k"].shape == (w.Hkv, w.N, w.d)
+    assert x["do"].shape == (w.Hq, w.N, w.d)
+    assert x["cu_seqlens"].tolist()[-1] == w.N
+    # the packed draw is the [1, H, T, d] draw of the same seed
+    from synth_inputs import Workload
+    small = Workload("pack-small", 1, 2, 1, 64, 8, (True,), seed=3, with_grad=True, pack=(4, 16))
+    p, y = make_inputs(small), make_custom_inputs(1, 2, 1, 64, 8, seed=3, with_grad=True)
+    for name in ("q", "k", "v", "do"):
+        assert (p[name] == y[name][0]).all()
+    assert p["cu_seqlens"].tolist()[-1] == 64 and len(p["cu_seqlens"]) == len(small.lengths()) + 1

@@ -41,6 +41,11 @@ MUTANTS = {
     "window_off_by_one_right": ("(dist > int(window))", "(dist >= int(window))"),
     "window_left_side_only": ("(dist < -int(window)) | (dist > int(window))", "(dist < -int(window))"),
     "window_ignored": ("if window is not None:\n        dist", "if False:\n        dist"),
+    "varlen_keys_leak_from_earlier_sequences": (
+        "ob, lb = attention_forward(q[None, :, s0:s1], k[None, :, s0:s1], v[None, :, s0:s1],",
+        "ob, lb = attention_forward(q[None, :, s0:s1], k[None, :, :s1], v[None, :, :s1],"),
+    "varlen_skips_first_sequence": ("for s0, s1 in zip(cu, cu[1:]):", "for s0, s1 in zip(cu[1:], cu[2:]):"),
+    "varlen_dk_dv_swapped": ("g[0][0], g[1][0], g[2][0]", "g[0][0], g[2][0], g[1][0]"),
 }
 
 
@@ -90,6 +95,19 @@ def pins_pass(mod) -> bool:
                 bo, bl = bf_forward(q, k, v, causal, 0.37, window=w)
                 if not (torch.allclose(o, torch.tensor(bo, dtype=torch.float64), atol=1e-11)
                         and torch.allclose(lse, torch.tensor(bl, dtype=torch.float64), atol=1e-11)):
+                    return False
+            # packed batch of sequences 3, 0, 4, 2 against the same-sequence-masked brute force
+            pq, pk, pv, pdo = q[0, :, :9], k[0, :, :9], v[0, :, :9], do[0, :, :9]
+            cu, seg = [0, 3, 3, 7, 9], [0, 0, 0, 2, 2, 2, 2, 3, 3]
+            o, lse = mod.varlen_forward(pq, pk, pv, cu, causal, 0.37)
+            bo, bl = bf_forward(pq[None], pk[None], pv[None], causal, 0.37, segments=seg)
+            if not (torch.allclose(o, torch.tensor(bo, dtype=torch.float64)[0], atol=1e-11)
+                    and torch.allclose(lse, torch.tensor(bl, dtype=torch.float64)[0], atol=1e-11)):
+                return False
+            g = mod.varlen_backward(pq, pk, pv, pdo, cu, causal, 0.37)
+            bg = bf_backward(pq[None], pk[None], pv[None], pdo[None], causal, 0.37, segments=seg)
+            for x, y in zip(g, bg):
+                if not torch.allclose(x, torch.tensor(y, dtype=torch.float64)[0], atol=1e-10):
                     return False
     except Exception:
         return False
