@@ -34,7 +34,7 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s (causal bf16, d=128) at N=8K–32K; % of MFMA bf16 peak"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
-BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K", "decode-32K")
+BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K", "decode-32K", "varlen-32K")
 PEAK_HBM_GBPS = 8000.0
 
 
@@ -157,24 +157,40 @@ def cpu_baseline(w, x, n_heads):
     """Time the fp64 oracle on the first n_heads query heads (batch 0, full N)."""
     import torch
 
-    from oracle import attention_backward, attention_forward
+    from oracle import attention_backward, attention_forward, varlen_backward, varlen_forward
     from synth_inputs import bf16_bits_to_f64
 
     hq = max(1, min(n_heads, w.Hq))
     hk = max(1, hq // w.group)            # the K/V heads those query heads read
     nb = w.B if w.nq is not None else 1   # decoding is cheap enough to take every sequence
+    threads = torch.get_num_threads()
+    pairs = nb * hq * w.keys_per_query(True)
+    flops = (4 * w.d + (10 * w.d if w.with_grad else 0)) * pairs
+    what = "forward + backward" if w.with_grad else "forward"
+    if w.pack is not None:
+        # packed batch: every sequence of the first hq query heads
+        sl = lambda name, h: torch.from_numpy(bf16_bits_to_f64(x[name][:h].copy()))
+        q, k, v = sl("q", hq), sl("k", hk), sl("v", hk)
+        cu = x["cu_seqlens"].tolist()
+        t0 = time.perf_counter()
+        varlen_forward(q, k, v, cu, True)
+        if w.with_grad:
+            varlen_backward(q, k, v, sl("do", hq), cu, True)
+        dt = time.perf_counter() - t0
+        return {
+            "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle {what} on query heads 0..{hq - 1} of {w.Hq}, every packed "
+                      f"sequence ({len(cu) - 1}, T={w.N}), same seeded inputs (algorithmic "
+                      f"{flops:.3g} FLOP in {dt:.2f} s; the oracle evaluates full masked rows)",
+            "host": platform.processor() or platform.machine(),
+        }
     sl = lambda name, h: torch.from_numpy(bf16_bits_to_f64(x[name][:nb, :h].copy()))
     q, k, v = sl("q", hq), sl("k", hk), sl("v", hk)
-    threads = torch.get_num_threads()
     t0 = time.perf_counter()
     attention_forward(q, k, v, True, window=w.window)
-    pairs = nb * hq * w.keys_per_query(True)
-    flops = 4 * w.d * pairs
     if w.with_grad:
         attention_backward(q, k, v, sl("do", hq), True, window=w.window)
-        flops += 10 * w.d * pairs
     dt = time.perf_counter() - t0
-    what = "forward + backward" if w.with_grad else "forward"
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -226,15 +242,22 @@ def main():
     q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     o = torch.empty_like(q)
     nq = w.N if w.nq is None else w.nq
-    lse = torch.empty((w.B, w.Hq, nq), dtype=torch.float32, device="cuda")
+    packed = w.pack is not None
+    # packed batches are [H, T, d] with LSE and D [H, T]
+    row_shape = (w.Hq, w.N) if packed else (w.B, w.Hq, nq)
+    lse = torch.empty(row_shape, dtype=torch.float32, device="cuda")
     decode = w.nq is not None
+    if packed:
+        lengths = w.lengths()
+        cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+        max_len = max(lengths)
     if decode:
         ws = torch.empty(attn.decode_workspace_bytes(w.B, w.Hq, w.Hkv, nq, w.N, w.d), dtype=torch.uint8,
                          device="cuda")
     if w.with_grad:
         do = dev(x["do"])
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        delta = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+        delta = torch.empty(row_shape, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     # Each phase is one kernel launch (the decode phase: the split kernel and
@@ -250,10 +273,19 @@ def main():
         mark(0)
         if decode:
             attn.fwd_decode(q, k, v, causal=True, out=o, lse=lse, workspace=ws, stream=stream)
+        elif packed:
+            attn.fwd_varlen(q, k, v, cu, max_len, causal=True, out=o, lse=lse, stream=stream)
         else:
             attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream, window=w.window)
         mark(1)
-        if w.with_grad:
+        if w.with_grad and packed:
+            # the pre-pass over packed rows is the plain one with B = 1, N = T
+            attn.bwd_preprocess(o[None], do[None], delta[None], stream=stream)
+            mark(2)
+            attn.bwd_grads_varlen(q, k, v, do, lse, delta, cu, max_len, causal=True, dq=dq, dk=dk,
+                                  dv=dv, stream=stream)
+            mark(3)
+        elif w.with_grad:
             attn.bwd_preprocess(o, do, delta, stream=stream)
             mark(2)
             attn.bwd_grads(q, k, v, do, lse, delta, causal=True, dq=dq, dk=dk, dv=dv,
@@ -342,14 +374,15 @@ def main():
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": True, "pass": "fwd+bwd" if w.with_grad else ("decode" if decode else "fwd"),
                    "flops_per_step": step_flops, "seed": w.seed, "input_scale": w.in_scale,
-                   "window": w.window, "queries": nq},
+                   "window": w.window, "queries": nq,
+                   "packed_lengths": w.lengths() if packed else None},
         "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
         "parts": parts,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1,
-                         "decode-32K": 32}[w.name]
+                         "decode-32K": 32, "varlen-32K": 3}[w.name]
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_heads or default_heads)
     print(json.dumps(result), flush=True)
 

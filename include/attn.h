@@ -195,6 +195,51 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * Packed variable-length batches (page "从“算力黑洞”到“效率革命”：大模型Attention的
+ * 演进之路", §6, scenario 2: long-context training data is built by
+ * concatenating and packing sequences).  B sequences of different lengths are
+ * stored back to back without padding; each is its own attention problem (its
+ * queries see only its own keys, positions counted from its first token), so
+ * the result equals B separate attn_fwd / attn_bwd calls.
+ *
+ *   q, o, dout, dq  [Hq,  total, d] bf16    k, v, dk, dv  [Hkv, total, d] bf16
+ *   lse             [Hq,  total]   fp32     (natural log of the scaled scores)
+ *   cu_seqlens      B + 1 int32 in DEVICE memory: sequence b is rows
+ *                   cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head;
+ *                   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = total
+ *                   (empty sequences allowed)
+ *   max_seqlen      the longest sequence (sizes the grid): 1 <= max_seqlen <= total
+ *   window < 0: none; >= 0: as attn_fwd_window, within each sequence
+ *   workspace       attn_bwd_varlen: >= attn_bwd_varlen_workspace_bytes(Hq, total, d)
+ *                   bytes (fp32 D per packed query row); contents on exit unspecified
+ *
+ * The boundaries live on the device and are not read by the host.  A table
+ * that breaks the rules above (or a sequence longer than max_seqlen) cannot
+ * make the kernels access memory outside the [H, total, d] tensors -- every
+ * boundary is clamped to [0, total] and every length to max_seqlen -- but the
+ * rows it describes wrongly are left unspecified.  total = 0 is an empty batch
+ * and returns ATTN_OK without touching memory.  Other errors as attn_fwd /
+ * attn_bwd (ATTN_ERR_SHAPE also for max_seqlen > total, or total * d or
+ * Hq * total beyond 2^31 - 1).  Deterministic, like the fixed-length calls.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int B, int total, int max_seqlen, int Hq, int Hkv,
+                    int d, int causal, int window, float scale, void* stream);
+size_t attn_bwd_varlen_workspace_bytes(int Hq, int total, int d);
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens, void* workspace, size_t workspace_bytes,
+                    int B, int total, int max_seqlen, int Hq, int Hkv, int d, int causal,
+                    int window, float scale, void* stream);
+/* The gradient stage of attn_bwd_varlen alone (dK/dV and dQ in one launch), for
+ * callers that run the D pre-pass themselves: over packed rows that pass is
+ * attn_bwd_preprocess with B = 1, N = total (delta is fp32 [Hq, total]). */
+int attn_bwd_grads_varlen(const void* q, const void* k, const void* v, const void* dout,
+                          const float* lse, const float* delta, void* dq, void* dk, void* dv,
+                          const int* cu_seqlens, int B, int total, int max_seqlen, int Hq,
+                          int Hkv, int d, int causal, int window, float scale, void* stream);
+
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
  * of the last failure on the calling thread.  Never NULL. */
 const char* attn_strerror(int code);

@@ -8,6 +8,7 @@ raises.
 
     o, lse = fwd(q, k, v, causal=True)           # q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    o, lse = fwd_varlen(q, k, v, cu_seqlens)     # packed q [Hq,T,d], k/v [Hkv,T,d]
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ import torch  # loads the HIP runtime that libattn.so then binds to
 
 __all__ = [
     "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads", "fwd_decode",
-    "decode_workspace_bytes",
+    "decode_workspace_bytes", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
+    "bwd_grads_varlen",
     "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
 ]
@@ -29,7 +31,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess",
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads", "attn_strerror",
             "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window",
-            "attn_fwd_decode", "attn_fwd_decode_workspace_bytes")
+            "attn_fwd_decode", "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
+            "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes", "attn_bwd_grads_varlen")
 
 ATTN_OK = 0
 
@@ -75,6 +78,16 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_decode.restype = i
     L.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_fwd_decode_workspace_bytes.restype = sz
+    L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_varlen.restype = i
+    L.attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i,
+                                  i, i, f, vp]
+    L.attn_bwd_varlen.restype = i
+    L.attn_bwd_grads_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                        i, i, f, vp]
+    L.attn_bwd_grads_varlen.restype = i
+    L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
+    L.attn_bwd_varlen_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_strerror.argtypes = [i]
@@ -316,3 +329,122 @@ def fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool =
         raise AttnError(rc, "attn_fwd_decode")
     return out, lse
 
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length batches
+# ---------------------------------------------------------------------------
+def _packing(cu_seqlens, max_seqlen: Optional[int], total: int, device) -> Tuple[torch.Tensor, int, int]:
+    """(int32 device boundaries, B, max_seqlen).  A host table, or a missing
+    max_seqlen, is checked here (it must rise from 0 to total); a device table
+    with max_seqlen given is passed on unread (the library clamps every
+    access, see include/attn.h)."""
+    if not torch.is_tensor(cu_seqlens):
+        cu_seqlens = torch.tensor(list(cu_seqlens), dtype=torch.int32)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of B + 1 boundaries")
+    if not cu_seqlens.is_cuda or max_seqlen is None:
+        cu = cu_seqlens.cpu().tolist()
+        if cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+            raise ValueError(f"cu_seqlens must rise from 0 to {total}")
+        longest = max(b - a for a, b in zip(cu, cu[1:]))
+        if max_seqlen is None:
+            max_seqlen = longest
+        elif max_seqlen < longest:
+            raise ValueError(f"max_seqlen {max_seqlen} < longest sequence {longest}")
+    return cu_seqlens.to(device).contiguous(), cu_seqlens.numel() - 1, int(max_seqlen)
+
+
+def bwd_varlen_workspace_bytes(Hq: int, total: int, d: int) -> int:
+    return int(lib().attn_bwd_varlen_workspace_bytes(Hq, total, d))
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
+               max_seqlen: Optional[int] = None, causal: bool = True,
+               scale: Optional[float] = None, window: Optional[int] = None,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Packed batch: q [Hq, T, d], k/v [Hkv, T, d] bf16, sequence b = rows
+    cu_seqlens[b] .. cu_seqlens[b+1]-1.  Returns O [Hq, T, d] and LSE [Hq, T]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q and k must be [H, T, d]")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    _check_bf16("q", q, (Hq, T, d))
+    _check_bf16("k", k, (Hkv, T, d))
+    _check_bf16("v", v, (Hkv, T, d))
+    cu, B, max_seqlen = _packing(cu_seqlens, max_seqlen, T, q.device)
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, (Hq, T, d))
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    _check_f32("lse", lse, (Hq, T))
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu), B, T,
+                               max_seqlen, Hq, Hkv, d, int(bool(causal)),
+                               -1 if window is None else int(window), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_varlen")
+    return out, lse
+
+
+def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+               lse: torch.Tensor, do: torch.Tensor, cu_seqlens, max_seqlen: Optional[int] = None,
+               causal: bool = True, scale: Optional[float] = None, window: Optional[int] = None,
+               dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+               dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ [Hq, T, d], dK and dV [Hkv, T, d] of a packed batch (see fwd_varlen)."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q and k must be [H, T, d]")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    for name, t, shp in (("q", q, (Hq, T, d)), ("k", k, (Hkv, T, d)), ("v", v, (Hkv, T, d)),
+                         ("o", o, (Hq, T, d)), ("do", do, (Hq, T, d))):
+        _check_bf16(name, t, shp)
+    _check_f32("lse", lse, (Hq, T))
+    cu, B, max_seqlen = _packing(cu_seqlens, max_seqlen, T, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(bwd_varlen_workspace_bytes(Hq, T, d), 16), dtype=torch.uint8,
+                                device=q.device)
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(cu), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), B, T, max_seqlen,
+                               Hq, Hkv, d, int(bool(causal)), -1 if window is None else int(window),
+                               tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_varlen")
+    return dq, dk, dv
+
+
+def bwd_grads_varlen(q, k, v, do, lse, delta, cu_seqlens, max_seqlen: Optional[int] = None,
+                     causal: bool = True, scale: Optional[float] = None,
+                     window: Optional[int] = None, dq=None, dk=None, dv=None,
+                     stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """The gradient stage of bwd_varlen given delta = rowsum(dO * O) [Hq, T]
+    (bwd_preprocess over the packed rows)."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q and k must be [H, T, d]")
+    Hq, T, d = q.shape
+    Hkv = k.shape[0]
+    for name, t, shp in (("q", q, (Hq, T, d)), ("k", k, (Hkv, T, d)), ("v", v, (Hkv, T, d)),
+                         ("do", do, (Hq, T, d))):
+        _check_bf16(name, t, shp)
+    _check_f32("lse", lse, (Hq, T))
+    _check_f32("delta", delta, (Hq, T))
+    cu, B, max_seqlen = _packing(cu_seqlens, max_seqlen, T, q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_bwd_grads_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
+                                     _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu), B, T, max_seqlen, Hq,
+                                     Hkv, d, int(bool(causal)),
+                                     -1 if window is None else int(window), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_bwd_grads_varlen")
+    return dq, dk, dv

@@ -269,6 +269,86 @@ ATTN_EXPORT int attn_fwd_decode(const void* q, const void* k, const void* v, voi
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd_decode launch");
 }
 
+// Shapes of a packed variable-length call: B sequences, `total` packed rows per
+// head, none longer than max_seqlen.  total == 0 is an empty batch.
+static int check_varlen(int B, int total, int max_seqlen, int Hq, int Hkv, int d) {
+  if (B <= 0 || total < 0 || max_seqlen < 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return ATTN_ERR_SHAPE;
+  if (Hq % Hkv != 0 || max_seqlen > total || (total > 0 && max_seqlen == 0)) return ATTN_ERR_SHAPE;
+  if ((long long)total * d > INT_MAX || (long long)Hq * total > INT_MAX) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+ATTN_EXPORT int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* cu_seqlens, int B, int total, int max_seqlen, int Hq,
+                                int Hkv, int d, int causal, int window, float scale,
+                                void* stream) {
+  int rc = check_varlen(B, total, max_seqlen, Hq, Hkv, d);
+  if (rc) return rc;
+  if ((rc = check_scale(scale))) return rc;
+  if (total == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if ((rc = current_device_check())) return rc;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen, d, causal != 0, scale,
+                  window < 0 ? -1 : window};
+  a.pack = attn::Packing{cu_seqlens, total};
+  hipError_t e = attn::launch_fwd(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd_varlen launch");
+}
+
+ATTN_EXPORT size_t attn_bwd_varlen_workspace_bytes(int Hq, int total, int d) {
+  if (Hq <= 0 || total < 0 || (long long)Hq * total > INT_MAX || (d != 64 && d != 128)) return 0;
+  return (size_t)Hq * total * sizeof(float);
+}
+
+ATTN_EXPORT int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                const int* cu_seqlens, void* workspace, size_t workspace_bytes,
+                                int B, int total, int max_seqlen, int Hq, int Hkv, int d,
+                                int causal, int window, float scale, void* stream) {
+  int rc = check_varlen(B, total, max_seqlen, Hq, Hkv, d);
+  if (rc) return rc;
+  if ((rc = check_scale(scale))) return rc;
+  if (total == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !cu_seqlens || !workspace)
+    return ATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes < (size_t)Hq * total * sizeof(float)) return ATTN_ERR_WORKSPACE;
+  if ((rc = current_device_check())) return rc;
+  attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace,
+                  B, Hq, Hkv, max_seqlen, d, causal != 0, scale, window < 0 ? -1 : window};
+  a.pack = attn::Packing{cu_seqlens, total};
+  hipError_t e = attn::launch_bwd(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_varlen launch");
+}
+
+ATTN_EXPORT int attn_bwd_grads_varlen(const void* q, const void* k, const void* v,
+                                      const void* dout, const float* lse, const float* delta,
+                                      void* dq, void* dk, void* dv, const int* cu_seqlens, int B,
+                                      int total, int max_seqlen, int Hq, int Hkv, int d,
+                                      int causal, int window, float scale, void* stream) {
+  int rc = check_varlen(B, total, max_seqlen, Hq, Hkv, d);
+  if (rc) return rc;
+  if ((rc = check_scale(scale))) return rc;
+  if (total == 0) return ATTN_OK;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !cu_seqlens)
+    return ATTN_ERR_NULL;
+  const void* ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if ((rc = current_device_check())) return rc;
+  attn::BwdArgs a{q, k, v, nullptr, lse, dout, dq, dk, dv, (float*)delta,
+                  B, Hq, Hkv, max_seqlen, d, causal != 0, scale, window < 0 ? -1 : window};
+  a.pack = attn::Packing{cu_seqlens, total};
+  hipError_t e = attn::launch_bwd_grads(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_grads_varlen launch");
+}
+
 ATTN_EXPORT const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";

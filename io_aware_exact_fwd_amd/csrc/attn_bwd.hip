@@ -83,8 +83,9 @@ template <int D, int NWK, bool CAUSAL, bool LOCAL>
 __device__ __forceinline__ void dkdv_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
-    float scale, float scale_log2, int xcd_remap, int window, int w, unsigned char* smem) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nmax, int BHkv, int Hq, int Hkv, int G,
+    float scale, float scale_log2, int xcd_remap, int window, const Packing& pk, int w,
+    unsigned char* smem) {
   using C = DkdvCfg<D, NWK>;
   constexpr int kPrefetch = 3;   // (A, B) fragment pairs in flight ahead of their MFMA
   constexpr int NW = C::kNW;
@@ -110,9 +111,15 @@ __device__ __forceinline__ void dkdv_block(
     kb = w / BHkv;
   }
   const int b = bhk / Hkv, hk = bhk - b * Hkv;
+  const SeqSpan sp = seq_span(pk, Nmax, b);
+  const int N = sp.len;                  // rows of this sequence
   const int k0 = kb * C::kBKV;
+  if (k0 >= N) return;                   // a block past a shorter packed sequence (uniform)
   const int kw0 = k0 + kg * 32;
-  const size_t kv_off = ((size_t)b * Hkv + hk) * N * D;
+  const size_t kv_off = sp.row0(pk, Nmax, b, hk, Hkv) * D;
+  // rows of query head hk*G + hh start at q_row0 + hh * q_hstride
+  const size_t q_row0 = sp.row0(pk, Nmax, b, hk * G, Hq);
+  const size_t q_hstride = head_stride(pk, Nmax);
 
   unsigned char* Kt = smem + C::kK;
   unsigned char* Vt = smem + C::kV;
@@ -132,7 +139,7 @@ __device__ __forceinline__ void dkdv_block(
   TileLoader<D, BQ, NW> ldq;
   ldq.init(wave, lane);
   auto issue = [&](int hh, int qt, int buf) {
-    const size_t qh_off = ((size_t)b * Hq + hk * G + hh) * N * D;
+    const size_t qh_off = (q_row0 + hh * q_hstride) * D;
     ldq.load(Q + qh_off, qt * BQ, N, qtile(buf), wave);
     ldq.load(dO + qh_off, qt * BQ, N, qtile(buf) + C::kQTile, wave);
   };
@@ -146,7 +153,7 @@ __device__ __forceinline__ void dkdv_block(
     const int row = qt * BQ + (tid & (BQ - 1));
     stat_valid = tid < 2 * BQ && row < N;
     if (stat_valid) {
-      const size_t idx = ((size_t)b * Hq + hk * G + hh) * N + row;
+      const size_t idx = q_row0 + hh * q_hstride + row;
       stat_raw = (tid < BQ ? LSE : Dl)[idx];
     }
   };
@@ -313,10 +320,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int BHkv, int Hq, int Hkv, int G,
-    float scale, float scale_log2, int xcd_remap, int window) {
+    float scale, float scale_log2, int xcd_remap, int window, Packing pk) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
-                                    scale_log2, xcd_remap, window, blockIdx.x, smem);
+                                    scale_log2, xcd_remap, window, pk, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -336,8 +343,8 @@ template <int D, int BC, int NW, bool CAUSAL, bool LOCAL>
 __device__ __forceinline__ void dq_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
-    uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
-    float scale_log2, int xcd_remap, int window, int w, unsigned char* smem) {
+    uint16_t* __restrict__ dQ, int Nmax, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
+    float scale_log2, int xcd_remap, int window, const Packing& pk, int w, unsigned char* smem) {
   using C = DqCfg<D, BC, NW>;
   constexpr int kPrefetch = 6;   // K/V fragments in flight ahead of their MFMA
   constexpr int DS = D / 16;
@@ -358,9 +365,13 @@ __device__ __forceinline__ void dq_block(
   }
   const int qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
   const int b = bh / Hq, h = bh - b * Hq, hk = h / G;
-  const size_t q_off = (size_t)bh * N * D;
-  const size_t kv_off = ((size_t)b * Hkv + hk) * N * D;
+  const SeqSpan sp = seq_span(pk, Nmax, b);
+  const int N = sp.len;                  // rows of this sequence
   const int q0 = qb * C::kBQ;
+  if (q0 >= N) return;                   // a block past a shorter packed sequence (uniform)
+  const size_t q_row0 = sp.row0(pk, Nmax, b, h, Hq);
+  const size_t q_off = q_row0 * D;
+  const size_t kv_off = sp.row0(pk, Nmax, b, hk, Hkv) * D;
   const int qw0 = q0 + wave * 32;
   const int q = qw0 + l32;              // this lane's query row
   const bool wave_live = qw0 < N;
@@ -371,8 +382,8 @@ __device__ __forceinline__ void dq_block(
     qf[s] = q < N ? *(const u32x4*)(Q + q_off + (size_t)q * D + s * 16 + 8 * hi) : zero4();
     dof[s] = q < N ? *(const u32x4*)(dO + q_off + (size_t)q * D + s * 16 + 8 * hi) : zero4();
   }
-  const float lse_l2 = q < N ? LSE[(size_t)bh * N + q] * kLog2e : INFINITY;
-  const float del = q < N ? Dl[(size_t)bh * N + q] : 0.f;
+  const float lse_l2 = q < N ? LSE[q_row0 + q] * kLog2e : INFINITY;
+  const float del = q < N ? Dl[q_row0 + q] : 0.f;
 
   f32x16 dqT[DB];
 #pragma unroll
@@ -482,10 +493,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale,
-    float scale_log2, int xcd_remap, int window) {
+    float scale_log2, int xcd_remap, int window, Packing pk) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   dq_block<D, BC, NW, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
-                                     scale_log2, xcd_remap, window, blockIdx.x, smem);
+                                     scale_log2, xcd_remap, window, pk, blockIdx.x, smem);
 }
 
 // dK/dV and dQ in one launch: workgroups [0, n_dkdv) are dK/dV blocks and the
@@ -499,16 +510,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
     int BHkv, int BH, int Hq, int Hkv, int G, int n_dkdv, int n_qb, float scale, float scale_log2,
-    int xcd_kv, int xcd_q, int window) {
+    int xcd_kv, int xcd_q, int window, Packing pk) {
   static_assert(2 * NWK == NW, "both halves run the same number of waves");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int w = blockIdx.x;
   if (w < n_dkdv)
     dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
-                                      scale_log2, xcd_kv, window, w, smem);
+                                      scale_log2, xcd_kv, window, pk, w, smem);
   else
     dq_block<D, BC, NW, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
-                                       scale_log2, xcd_q, window, w - n_dkdv, smem);
+                                       scale_log2, xcd_q, window, pk, w - n_dkdv, smem);
 }
 
 template <typename KernelT>
@@ -518,7 +529,7 @@ hipError_t allow_lds(KernelT kern, int bytes) {
 
 template <int D>
 hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
-  const int rows = a.B * a.Hq * a.N;
+  const int rows = (int)a.rows();   // the host checks that it fits
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, stream,
                      (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
@@ -545,7 +556,7 @@ struct LaunchDkdv {
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
                        a.N, BHkv, a.Hq, a.Hkv, a.Hq / a.Hkv, a.scale, a.scale * kLog2e,
-                       BHkv % 8 == 0 ? 1 : 0, a.window);
+                       xcd_remap(BHkv, a.pack), a.window, a.pack);
     return hipGetLastError();
   }
 };
@@ -564,8 +575,8 @@ struct LaunchDq {
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CQ::kThreads), CQ::kLdsBytes, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, BH, a.Hq,
-                       a.Hkv, a.Hq / a.Hkv, n_qb, a.scale, a.scale * kLog2e, BH % 8 == 0 ? 1 : 0,
-                       a.window);
+                       a.Hkv, a.Hq / a.Hkv, n_qb, a.scale, a.scale * kLog2e, xcd_remap(BH, a.pack),
+                       a.window, a.pack);
     return hipGetLastError();
   }
 };
@@ -590,8 +601,8 @@ struct LaunchGrads {
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,
                        (uint16_t*)a.dv, a.N, BHkv, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, (int)n_dkdv,
-                       n_qb, a.scale, a.scale * kLog2e, BHkv % 8 == 0 ? 1 : 0,
-                       BH % 8 == 0 ? 1 : 0, a.window);
+                       n_qb, a.scale, a.scale * kLog2e, xcd_remap(BHkv, a.pack),
+                       xcd_remap(BH, a.pack), a.window, a.pack);
     return hipGetLastError();
   }
 };

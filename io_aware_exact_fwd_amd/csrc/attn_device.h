@@ -75,9 +75,37 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 }  // namespace attn
 
+#include "attn_launch.h"
 #include "attn_layout.h"
 
 namespace attn {
+
+// The rows one (batch, head) pair owns.  Fixed length ([B, H, N, d]): rows
+// (b H + h) N .. + N - 1.  Packed ([H, T, d], see Packing): rows h T + cu[b]
+// .. h T + cu[b+1] - 1.  Boundaries are clamped to [0, T] and lengths to N,
+// so a malformed table cannot move an access outside the tensors (its rows
+// are then simply not all computed).  b is uniform, so the two boundary reads
+// are scalar loads.
+struct SeqSpan {
+  int start;  // first row of the sequence within each head's rows (0: fixed length)
+  int len;    // rows (queries and keys) of the sequence
+  // first row of head h (of H) for batch b
+  __device__ __forceinline__ size_t row0(const Packing& p, int N, int b, int h, int H) const {
+    return p.cu ? (size_t)h * p.T + start : ((size_t)b * H + h) * N;
+  }
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const Packing& p, int N, int b) {
+  if (!p.cu) return SeqSpan{0, N};
+  const int c0 = min(max(p.cu[b], 0), p.T);
+  const int c1 = min(max(p.cu[b + 1], c0), p.T);
+  return SeqSpan{c0, min(c1 - c0, N)};
+}
+
+// Row distance between consecutive heads of one batch (N, or T when packed).
+__device__ __forceinline__ size_t head_stride(const Packing& p, int N) {
+  return p.cu ? (size_t)p.T : (size_t)N;
+}
 
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;

@@ -65,8 +65,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
-    int N, int BH, int Hq, int Hkv, int G, int n_qb, float scale_log2, int xcd_remap,
-    int window) {
+    int Nmax, int BH, int Hq, int Hkv, int G, int n_qb, float scale_log2, int xcd_remap,
+    int window, Packing pk) {
   using C = FwdCfg<D, BC, NW>;
   constexpr int kPrefetch = 6; // K fragments in flight ahead of their MFMA
   constexpr int DS = D / 16;   // k-slabs of the QK^T contraction
@@ -97,11 +97,17 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const int b = bh / Hq;
   const int h = bh - b * Hq;
   const int hk = h / G;
-  const uint16_t* Qp = Q + (size_t)bh * N * D;
-  const uint16_t* Kp = K + ((size_t)b * Hkv + hk) * N * D;
-  const uint16_t* Vp = V + ((size_t)b * Hkv + hk) * N * D;
-
+  // this pair's sequence: N rows of queries and keys (packed: its own length)
+  const SeqSpan sp = seq_span(pk, Nmax, b);
+  const int N = sp.len;
   const int q0 = qb * C::kBR;
+  if (q0 >= N) return;   // a block past a shorter packed sequence (uniform)
+  const size_t q_row0 = sp.row0(pk, Nmax, b, h, Hq);
+  const size_t kv_row0 = sp.row0(pk, Nmax, b, hk, Hkv);
+  const uint16_t* Qp = Q + q_row0 * D;
+  const uint16_t* Kp = K + kv_row0 * D;
+  const uint16_t* Vp = V + kv_row0 * D;
+
   const int qw0 = q0 + wave * 32;  // first query row of this wave
   const int qw1 = qw0 + 31;        // last query row of this wave
   const bool wave_live = qw0 < N;
@@ -254,7 +260,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const float inv = 1.f / lt;
   const int q = qw0 + l32;
   if (q < N) {
-    uint16_t* orow = O + ((size_t)bh * N + q) * D;
+    uint16_t* orow = O + (q_row0 + q) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -264,7 +270,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
         *(u32x2*)(orow + d0) = u32x2{pack_bf16x2(a[4 * r + 0] * inv, a[4 * r + 1] * inv),
                                      pack_bf16x2(a[4 * r + 2] * inv, a[4 * r + 3] * inv)};
       }
-    if (hi == 0) LSE[(size_t)bh * N + q] = (m_run + log2_fast(lt)) * kLn2;
+    if (hi == 0) LSE[q_row0 + q] = (m_run + log2_fast(lt)) * kLn2;
   }
 }
 
@@ -280,11 +286,11 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  const int xcd_remap = (BH % 8 == 0) ? 1 : 0;
+  const int remap = xcd_remap(BH, a.pack);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (uint16_t*)a.o, a.lse, a.N, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, n_qb,
-                     a.scale * kLog2e, xcd_remap, a.window);
+                     a.scale * kLog2e, remap, a.window, a.pack);
   return hipGetLastError();
 }
 

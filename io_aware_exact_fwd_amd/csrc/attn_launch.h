@@ -6,6 +6,23 @@
 
 namespace attn {
 
+// Packed variable-length batches: tensors are [H, T, d] with the B sequences
+// concatenated along T, and sequence b is rows cu[b] .. cu[b+1]-1 of every
+// head (LSE and D: [H, T]).  cu == nullptr means fixed-length [B, H, N, d]
+// tensors.  With a packing, N is the longest sequence (it sizes the grid).
+struct Packing {
+  const int* cu = nullptr;  // B + 1 boundaries, device memory
+  int T = 0;                // packed rows per head
+};
+
+// Whether a grid over `units` (batch, head) pairs keeps all blocks of a pair
+// on one XCD (workgroup w runs on XCD w % 8).  That keeps a pair's K/V tiles in
+// one L2 and balances the XCDs when every pair carries the same work.  Packed
+// batches do not (pairs of a long sequence carry more), so they keep the plain
+// order, where block w goes to XCD (w mod units) mod 8: with units a multiple
+// of 8 each XCD then gets the same heads of every sequence.
+inline int xcd_remap(int units, const Packing& p) { return (units % 8 == 0 && !p.cu) ? 1 : 0; }
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -16,6 +33,7 @@ struct FwdArgs {
   bool causal;
   float scale;
   int window = -1;  // sliding window: keys with |i - j| <= window; < 0 = none
+  Packing pack;
 };
 
 struct BwdArgs {
@@ -28,11 +46,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: D_i = rowsum(dO * O), fp32 [B, Hq, N]
+  float* delta;  // workspace: D_i = rowsum(dO * O), fp32 [B, Hq, N] (packed: [Hq, T])
   int B, Hq, Hkv, N, d;
   bool causal;
   float scale;
   int window = -1;  // sliding window: keys with |i - j| <= window; < 0 = none
+  Packing pack;
+  // query rows over all heads: B*Hq*N, or Hq*T when packed
+  size_t rows() const { return pack.cu ? (size_t)Hq * pack.T : (size_t)B * Hq * N; }
 };
 
 // Bytes of workspace the backward uses (fp32 D per query row).

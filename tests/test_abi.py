@@ -34,7 +34,9 @@ def test_header_declares_the_boundary():
                                            "attn_device_check", "attn_fwd_window",
                                            "attn_bwd_window", "attn_bwd_grads_window",
                                            "attn_fwd_decode",
-                                           "attn_fwd_decode_workspace_bytes"])
+                                           "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
+                                           "attn_bwd_varlen", "attn_bwd_grads_varlen",
+                                           "attn_bwd_varlen_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -184,3 +186,36 @@ def test_decode_validation_and_workspace(L):
     assert L.attn_fwd_decode(*args, 1, 4, 4, 1, 64, 64, 1, -1, -1.0, 0, A, 1 << 20, None) == 5
     assert L.attn_fwd_decode(A, A, MIS, A, A, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, A, 1 << 20, None) == 3
 
+
+
+def test_varlen_validation_and_workspace(L):
+    """Packed batches: shape rules, the empty batch, workspace size, all
+    before any device work."""
+    assert L.attn_bwd_varlen_workspace_bytes(8, 1000, 128) == 8 * 1000 * 4
+    assert L.attn_bwd_varlen_workspace_bytes(8, 1000, 96) == 0
+    assert L.attn_bwd_varlen_workspace_bytes(0, 1000, 128) == 0
+    f = L.attn_fwd_varlen
+    #         q  k  v  o  lse cu   B  T    max Hq Hkv d  causal win scale
+    assert f(A, A, A, A, A, A, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) in (3, 6)   # valid: no device
+    assert f(A, A, A, A, A, A, 0, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 2        # B = 0
+    assert f(A, A, A, A, A, A, 2, 100, 101, 4, 2, 64, 1, -1, 0.1, None) == 2       # max > total
+    assert f(A, A, A, A, A, A, 2, 100, 0, 4, 2, 64, 1, -1, 0.1, None) == 2         # max = 0 < total
+    assert f(A, A, A, A, A, A, 2, 100, 60, 4, 3, 64, 1, -1, 0.1, None) == 2        # Hq % Hkv
+    assert f(A, A, A, A, A, A, 2, 100, 60, 4, 2, 96, 1, -1, 0.1, None) == 3        # d
+    assert f(A, A, A, A, A, None, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 1     # no table
+    assert f(A, A, MIS, A, A, A, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 3      # alignment
+    assert f(A, A, A, A, A, A, 2, 100, 60, 4, 2, 64, 1, -1, 0.0, None) == 5        # scale
+    assert f(None, None, None, None, None, None, 3, 0, 0, 4, 2, 64, 1, -1, 0.1, None) == 0  # empty batch
+    assert f(A, A, A, A, A, A, 2, 1 << 25, 60, 4, 2, 128, 1, -1, 0.1, None) == 2   # total * d > 2^31
+    b = L.attn_bwd_varlen
+    ptrs = [A] * 10
+    assert b(*ptrs, A, 4 * 100 * 4, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) in (3, 6)
+    assert b(*ptrs, A, 4 * 100 * 4 - 1, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 4
+    assert b(*ptrs[:9], None, A, 1 << 20, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 1
+    assert b(*ptrs, A, 1 << 20, 2, 100, 200, 4, 2, 64, 1, -1, 0.1, None) == 2
+    assert b(*([None] * 10), None, 0, 2, 0, 0, 4, 2, 64, 1, -1, 0.1, None) == 0
+    g = L.attn_bwd_grads_varlen
+    assert g(*([A] * 10), 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) in (3, 6)
+    assert g(*([A] * 9), None, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 1
+    assert g(*([A] * 10), 2, 100, 60, 4, 2, 64, 1, -1, -2.0, None) == 5
+    assert g(*([A] * 5), MIS, *([A] * 4), 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 3
