@@ -63,7 +63,9 @@ def source_sha(kernel: str) -> str:
 
 
 def _per_kernel(csv_path: str, counter: str):
-    """Average value of one counter per dispatch, by kernel short name."""
+    """Average value of one counter per dispatch, by kernel short name.  For the
+    copy kernel, the largest dispatch: the calibration copy, not the small
+    uploads of the inputs that run through the same kernel."""
     import csv
     import collections
     acc = collections.defaultdict(list)
@@ -75,7 +77,7 @@ def _per_kernel(csv_path: str, counter: str):
             short = next((k for k in KERNEL_SOURCES if k in name), COPY_KERNEL if COPY_KERNEL in name else None)
             if short:
                 acc[short].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+    return {k: (max(v) if k == COPY_KERNEL else sum(v) / len(v)) for k, v in acc.items()}
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str,
