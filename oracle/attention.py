@@ -87,6 +87,7 @@ __all__ = [
     "attention_backward",
     "attention_probs",
     "forward_rows",
+    "probs_rows",
     "backward_dq_rows",
     "varlen_forward",
     "varlen_backward",
@@ -208,6 +209,19 @@ def forward_rows(q, k, v, causal: bool, scale: Optional[float], b: int, h: int,
     k_g, v_g = to_f64(k[b, g]), to_f64(v[b, g])
     p, lse = _row_probs(q_r, k_g, rows_t + (k.shape[2] - q.shape[2]), causal, tau, window)
     return p @ v_g, lse
+
+
+def probs_rows(q, k, causal: bool, scale: Optional[float], b: int, h: int,
+               rows: Sequence[int]) -> torch.Tensor:
+    """Rows of the probability matrix P [len(rows), N_k] of one (batch, query head)."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = h // (Hq // Hkv)
+    d = q.shape[-1]
+    tau = default_scale(d) if scale is None else float(scale)
+    rows_t = torch.as_tensor(list(rows), dtype=torch.int64)
+    p, _ = _row_probs(to_f64(q[b, h])[rows_t], to_f64(k[b, g]), rows_t + (k.shape[2] - q.shape[2]),
+                      causal, tau, None)
+    return p
 
 
 def attention_backward(q, k, v, do, causal: bool, scale: Optional[float] = None,

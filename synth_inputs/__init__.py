@@ -19,6 +19,10 @@ generator ``PCG64(seed)`` draws ``exp(uniform(ln lo, ln hi))`` rounded to an
 integer, one length at a time, until the pack holds T tokens (the last length
 is cut to fit).
 
+8-bit inputs (OCP E4M3) draw the same fp32 values, then per (batch, head):
+``descale = max|x| / 448`` (fp32) and ``code = E4M3(x / descale)``, rounded to
+the nearest representable value, ties to even (``f32_to_e4m3_bits``).
+
 The bf16 payload is returned as ``uint16`` bit patterns; ``bf16_bits_to_f32``
 and ``bf16_bits_to_f64`` decode them exactly.
 """
@@ -41,6 +45,8 @@ __all__ = [
     "make_custom_inputs",
     "pack_lengths",
     "cu_from_lengths",
+    "f32_to_e4m3_bits",
+    "make_fp8_inputs",
 ]
 
 
@@ -64,6 +70,7 @@ class Workload:
     # packed variable-length batch: N tokens split into sequences whose lengths
     # are drawn log-uniform in [lo, hi] (pack_lengths with this seed); B = 1
     pack: Optional[Tuple[int, int]] = None
+    fp8: bool = False               # Q, K, V as E4M3 codes with per-head descales
 
     def lengths(self) -> List[int]:
         """Sequence lengths of a packed workload (one sequence of N otherwise)."""
@@ -122,6 +129,8 @@ WORKLOADS: Dict[str, Workload] = {
                  note="sliding-window causal attention, 4096 keys back"),
         Workload("decode-32K", 16, 32, 8, 32768, 128, (True,), seed=6, nq=1,
                  note="one new query per sequence against a 32768-key cache"),
+        Workload("fp8-8K", 1, 32, 32, 8192, 128, (True,), seed=8, fp8=True,
+                 note="E4M3 inputs with one descale per (batch, head)"),
         Workload("varlen-32K", 1, 8, 8, 32768, 128, (True,), seed=7, with_grad=True,
                  pack=(512, 16384),
                  note="32768 tokens packed from sequences of 512..16384 tokens (log-uniform)"),
@@ -141,6 +150,42 @@ def pack_lengths(total: int, seed: int, lo: int, hi: int) -> List[int]:
         n = min(max(n, 1), left)
         out.append(n)
         left -= n
+    return out
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to OCP E4M3 (nearest, ties to even); return uint8 codes.
+
+    Every value must round to at most 448 in magnitude (no saturation here).
+    The rounding works on the format's grid: spacing 2^-9 below 2^-6, and
+    2^(e-3) in the binade [2^e, 2^(e+1)).  The quotient by a power of two is
+    exact in float64, and numpy's rint rounds half to even.
+    """
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    neg = np.signbit(np.asarray(x, dtype=np.float64))
+    _, ex = np.frexp(np.maximum(a, 2.0 ** -6))       # a = f * 2^ex, f in [0.5, 1)
+    step = np.ldexp(1.0, ex - 1 - 3)
+    q = np.rint(a / step) * step
+    if bool((q > 448.0).any()):
+        raise ValueError("value beyond the E4M3 range (448)")
+    _, eq = np.frexp(np.where(q > 0, q, 1.0))
+    e_field = np.where(q >= 2.0 ** -6, eq - 1 + 7, 0)
+    mant = np.where(q >= 2.0 ** -6, q / np.ldexp(1.0, eq - 1 - 3) - 8, q / 2.0 ** -9)
+    code = (e_field.astype(np.int64) << 3) | np.rint(mant).astype(np.int64)
+    code = np.where(q == 0, 0, code) | (neg.astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+def make_fp8_inputs(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int) -> Dict[str, np.ndarray]:
+    """E4M3 codes for Q, K, V ([B, H, N, d] uint8) and their fp32 descales ([B, H])."""
+    x = make_custom_inputs(B, Hq, Hkv, N, d, seed, keep_f32=True)
+    out: Dict[str, np.ndarray] = {}
+    for name in ("q", "k", "v"):
+        f = x[name + "_f32"]
+        amax = np.abs(f).max(axis=(2, 3))
+        descale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        out[name + "8"] = f32_to_e4m3_bits(f.astype(np.float64) / descale.astype(np.float64)[:, :, None, None])
+        out[name + "_descale"] = descale
     return out
 
 
@@ -210,6 +255,8 @@ def make_inputs(workload: str | Workload, seed: Optional[int] = None,
     """Inputs of a named workload (its own seed unless ``seed`` is given)."""
     w = WORKLOADS[workload] if isinstance(workload, str) else workload
     sd = w.seed if seed is None else seed
+    if w.fp8:
+        return make_fp8_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, sd)
     if w.pack is not None:
         # packed batch: [H, T, d] tensors (the [1, H, T, d] draw) plus the boundaries
         x = make_custom_inputs(1, w.Hq, w.Hkv, w.N, w.d, sd, in_scale=w.in_scale,
