@@ -34,8 +34,11 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s (causal bf16, d=128) at N=8K–32K; % of MFMA bf16 peak"
 # MI355X published dense bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 FLOP/clk/CU.
 PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
-BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K", "decode-32K", "varlen-32K")
+BENCH_WORKLOADS = ("fb-32K", "fwd-8K", "gqa-16K", "fwd-2K", "swa-32K", "decode-32K", "varlen-32K",
+                   "fp8-8K")
 PEAK_HBM_GBPS = 8000.0
+# dense 8-bit (E4M3) MFMA peak: twice the bf16 rate per CU and clock
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 
 
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
@@ -49,6 +52,7 @@ KERNEL_SOURCES = {
     "bwd_dq_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
     "bwd_grads_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
     "attn_decode_split_kernel": ("attn_device.h", "attn_layout.h", "attn_decode.hip"),
+    "attn_fwd_fp8_kernel": ("attn_device.h", "attn_layout.h", "attn_fwd_fp8.hip"),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -159,7 +163,8 @@ def cpu_baseline(w, x, n_heads):
     """Time the fp64 oracle on the first n_heads query heads (batch 0, full N)."""
     import torch
 
-    from oracle import attention_backward, attention_forward, varlen_backward, varlen_forward
+    from oracle import (attention_backward, attention_forward, fp8_attention_forward, varlen_backward,
+                        varlen_forward)
     from synth_inputs import bf16_bits_to_f64
 
     hq = max(1, min(n_heads, w.Hq))
@@ -169,6 +174,19 @@ def cpu_baseline(w, x, n_heads):
     pairs = nb * hq * w.keys_per_query(True)
     flops = (4 * w.d + (10 * w.d if w.with_grad else 0)) * pairs
     what = "forward + backward" if w.with_grad else "forward"
+    if w.fp8:
+        sl8 = lambda name, h: x[name][:1, :h].copy()
+        t0 = time.perf_counter()
+        fp8_attention_forward(sl8("q8", hq), sl8("k8", hk), sl8("v8", hk), x["q_descale"][:1, :hq],
+                              x["k_descale"][:1, :hk], x["v_descale"][:1, :hk], True)
+        dt = time.perf_counter() - t0
+        return {
+            "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle forward of the dequantized E4M3 inputs on query heads 0..{hq - 1} "
+                      f"of {w.Hq}, full N={w.N}, same seeded inputs (algorithmic {flops:.3g} FLOP in "
+                      f"{dt:.2f} s; the oracle evaluates full masked rows)",
+            "host": platform.processor() or platform.machine(),
+        }
     if w.pack is not None:
         # packed batch: every sequence of the first hq query heads
         sl = lambda name, h: torch.from_numpy(bf16_bits_to_f64(x[name][:h].copy()))
@@ -241,7 +259,12 @@ def main():
     def dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
-    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    if w.fp8:
+        q8, k8, v8 = (torch.from_numpy(x[n]).cuda() for n in ("q8", "k8", "v8"))
+        q_ds, k_ds, v_ds = (torch.from_numpy(x[n]).cuda() for n in ("q_descale", "k_descale", "v_descale"))
+        q = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.bfloat16, device="cuda")   # O's shape
+    else:
+        q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
     o = torch.empty_like(q)
     nq = w.N if w.nq is None else w.nq
     packed = w.pack is not None
@@ -277,6 +300,8 @@ def main():
             attn.fwd_decode(q, k, v, causal=True, out=o, lse=lse, workspace=ws, stream=stream)
         elif packed:
             attn.fwd_varlen(q, k, v, cu, max_len, causal=True, out=o, lse=lse, stream=stream)
+        elif w.fp8:
+            attn.fwd_fp8(q8, k8, v8, q_ds, k_ds, v_ds, causal=True, out=o, lse=lse, stream=stream)
         else:
             attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream, window=w.window)
         mark(1)
@@ -322,13 +347,14 @@ def main():
     # blocks' second S and dP are recomputation and not counted); the pre-pass
     # does no matmul.
     per_pair = {"fwd": 4 * w.d, "bwd_pre": 0, "bwd_grads": 10 * w.d, "decode": 4 * w.d}
-    kernel_name = {"fwd": "attn_fwd_kernel", "bwd_pre": "bwd_pre_kernel",
+    kernel_name = {"fwd": "attn_fwd_fp8_kernel" if w.fp8 else "attn_fwd_kernel", "bwd_pre": "bwd_pre_kernel",
                    "bwd_grads": "bwd_grads_kernel", "decode": "attn_decode_split_kernel"}
     fwd_flops = w.fwd_flops(True)
     bwd_flops = w.bwd_flops(True) if w.with_grad else 0
     step_flops = fwd_flops + bwd_flops
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
+    mfma_peak = PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS
     parts = {}
     for i, ph in enumerate(phases):
         ms = [e[i].elapsed_time(e[i + 1]) for e in events]
@@ -336,7 +362,7 @@ def main():
         flops = per_pair[ph] * pairs
         parts[ph] = {"kernel": kernel_name[ph], "ms_avg": avg, "ms_median": float(np.median(ms)),
                      "algorithmic_flops": flops, "tflops": flops / (avg * 1e-3) / 1e12}
-        parts[ph]["pct_of_peak"] = 100 * parts[ph]["tflops"] / PEAK_BF16_TFLOPS
+        parts[ph]["pct_of_peak"] = 100 * parts[ph]["tflops"] / mfma_peak
     if w.with_grad:
         bwd_ms = sum(parts[p]["ms_avg"] for p in phases[1:])
         parts["bwd_total"] = {"ms_avg": bwd_ms, "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
@@ -355,8 +381,9 @@ def main():
                     "ms_per_launch": parts[dom]["ms_avg"], "algorithmic_bytes_per_launch": alg_bytes}
     else:
         achieved = parts[dom]["tflops"]
-        roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": kernel_name[dom],
+        peak = PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS
+        roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                    "frac": achieved / peak, "traffic": traffic, "kernel": kernel_name[dom],
                     "ms_per_launch": parts[dom]["ms_avg"],
                     "algorithmic_flops_per_launch": parts[dom]["algorithmic_flops"]}
 
@@ -371,20 +398,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if w.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": True, "pass": "fwd+bwd" if w.with_grad else ("decode" if decode else "fwd"),
                    "flops_per_step": step_flops, "seed": w.seed, "input_scale": w.in_scale,
                    "window": w.window, "queries": nq,
                    "packed_lengths": w.lengths() if packed else None},
-        "pct_of_peak": 100 * value / PEAK_BF16_TFLOPS,
+        "pct_of_peak": 100 * value / mfma_peak,
         "parts": parts,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1,
-                         "decode-32K": 32, "varlen-32K": 3}[w.name]
+                         "decode-32K": 32, "varlen-32K": 3, "fp8-8K": 16}[w.name]
         result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_sample_heads or default_heads)
     print(json.dumps(result), flush=True)
 

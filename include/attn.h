@@ -240,6 +240,31 @@ int attn_bwd_grads_varlen(const void* q, const void* k, const void* v, const voi
                           const int* cu_seqlens, int B, int total, int max_seqlen, int Hq,
                           int Hkv, int d, int causal, int window, float scale, void* stream);
 
+/*
+ * Forward over 8-bit inputs (page "6.1 2023 年代：長上下文擴展技術：FlashAttention、
+ * RoPE 與稀疏注意力", §2.3: FlashAttention-3's low-bit path; the method stays
+ * exact).  Q, K, V hold OCP E4M3 codes (1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits; largest value 448; S.1111.111 is NaN), one byte per
+ * element; element x of head (b, h) stands for decode(x) * descale[b, h].
+ * The result is the attention of those values, computed on the 8-bit matrix
+ * unit:
+ *
+ *   q          [B, Hq,  N, 128] E4M3, read       o   [B, Hq, N, 128] bf16, written
+ *   k, v       [B, Hkv, N, 128] E4M3, read       lse [B, Hq, N] fp32, written
+ *   q_descale  [B, Hq]  fp32, device, read;  k_descale, v_descale [B, Hkv] fp32, device, read
+ *
+ * The scores and their softmax statistics are fp32 (LSE as exact as the bf16
+ * forward's); the probabilities enter the P V product rounded to E4M3 after
+ * scaling by 2^8 (relative error <= 2^-4, absolute <= 2^-18 of the row's
+ * largest probability in the subnormal range), so |O - O_exact| <=
+ * sum_j max(2^-4 P_ij, 2^-18 max_k P_ik) |v_j| plus O's own bf16 rounding.
+ * NaN codes give NaN rows.  Errors as attn_fwd, with ATTN_ERR_UNSUPPORTED for
+ * d != 128.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                 const float* k_descale, const float* v_descale, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* stream);
+
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
  * of the last failure on the calling thread.  Never NULL. */
 const char* attn_strerror(int code);

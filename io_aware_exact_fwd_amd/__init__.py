@@ -22,7 +22,7 @@ import torch  # loads the HIP runtime that libattn.so then binds to
 __all__ = [
     "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads", "fwd_decode",
     "decode_workspace_bytes", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
-    "bwd_grads_varlen",
+    "bwd_grads_varlen", "fwd_fp8",
     "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
 ]
@@ -32,7 +32,8 @@ EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_prepro
             "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_grads", "attn_strerror",
             "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window",
             "attn_fwd_decode", "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
-            "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes", "attn_bwd_grads_varlen")
+            "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes", "attn_bwd_grads_varlen",
+            "attn_fwd_fp8")
 
 ATTN_OK = 0
 
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_grads_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
                                         i, i, f, vp]
     L.attn_bwd_grads_varlen.restype = i
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_fp8.restype = i
     L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
     L.attn_bwd_varlen_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -448,3 +451,34 @@ def bwd_grads_varlen(q, k, v, do, lse, delta, cu_seqlens, max_seqlen: Optional[i
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_bwd_grads_varlen")
     return dq, dk, dv
+
+
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_descale: torch.Tensor,
+            k_descale: torch.Tensor, v_descale: torch.Tensor, causal: bool = True,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """8-bit forward: q8 [B,Hq,N,128], k8/v8 [B,Hkv,N,128] E4M3 codes (uint8 or
+    float8_e4m3fn), descales fp32 [B,Hq] / [B,Hkv].  Returns O (bf16) and LSE (fp32)."""
+    if q8.dim() != 4 or k8.dim() != 4:
+        raise ValueError("q8 and k8 must be [B, H, N, d]")
+    B, Hq, N, d = q8.shape
+    Hkv = k8.shape[1]
+    for name, t, shp in (("q8", q8, (B, Hq, N, d)), ("k8", k8, (B, Hkv, N, d)), ("v8", v8, (B, Hkv, N, d))):
+        if t.element_size() != 1 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be a contiguous 1-byte CUDA tensor of shape {shp}")
+    _check_f32("q_descale", q_descale, (B, Hq))
+    _check_f32("k_descale", k_descale, (B, Hkv))
+    _check_f32("v_descale", v_descale, (B, Hkv))
+    if out is None:
+        out = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+    _check_bf16("out", out, (B, Hq, N, d))
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    _check_f32("lse", lse, (B, Hq, N))
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_descale), _ptr(k_descale),
+                            _ptr(v_descale), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d,
+                            int(bool(causal)), tau, _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_fp8")
+    return out, lse

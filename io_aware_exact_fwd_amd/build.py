@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 PROBE_SRC = "hbm_read_probe.hip"
 PROBE_PATH = os.path.join(PKG_DIR, "hbm_read_probe")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fwd_fp8.hip"]
 HEADERS = ["attn_device.h", "attn_launch.h", "attn_layout.h"]
 
 ARCH = "gfx950"

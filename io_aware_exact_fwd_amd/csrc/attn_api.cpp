@@ -349,6 +349,25 @@ ATTN_EXPORT int attn_bwd_grads_varlen(const void* q, const void* k, const void* 
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_grads_varlen launch");
 }
 
+ATTN_EXPORT int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                             const float* k_descale, const float* v_descale, void* o, float* lse,
+                             int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                             void* stream) {
+  if (!q || !k || !v || !q_descale || !k_descale || !v_descale || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_problem(B, Hq, Hkv, N, d);
+  if (rc) return rc;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  if ((rc = check_scale(scale))) return rc;
+  if ((rc = current_device_check())) return rc;
+  attn::Fp8FwdArgs a{q, k, v, q_descale, k_descale, v_descale, o, lse, B, Hq, Hkv, N, d,
+                     causal != 0, scale};
+  hipError_t e = attn::launch_fwd_fp8(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd_fp8 launch");
+}
+
 ATTN_EXPORT const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK: return "ok";

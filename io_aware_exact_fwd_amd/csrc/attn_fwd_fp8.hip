@@ -1,0 +1,273 @@
+// attn_fwd_fp8.hip -- forward of exact attention over 8-bit (OCP E4M3) inputs
+// on gfx950's 8-bit matrix unit (v_mfma_scale_f32_32x32x64_f8f6f4, unit
+// block scales).
+//
+// Page "6.1 2023 年代：長上下文擴展技術：FlashAttention、RoPE 與稀疏注意力", §2.3:
+// FlashAttention-3 adds a low-bit path, and the method stays exact.  Here Q, K
+// and V arrive as E4M3 codes, each (batch, head) with an fp32 descale factor;
+// the result is softmax attention of the dequantized values, O in bf16 and
+// LSE in fp32 as in the bf16 forward (page "6.1 …", §2.2).
+//
+// gfx950 mapping (d = 128; the structure of the bf16 forward in attn_fwd.hip):
+//   * one workgroup = 8 waves x 32 query rows of one (b, h), heaviest causal
+//     blocks first; 128-key K and V tiles of 16 KB each, double-buffered
+//     through direct 16-byte global -> LDS loads (an 8-bit row of 128 bytes
+//     has the layout of a d = 64 bf16 row, see attn_layout.h);
+//   * S^T = K Q^T per 32-key block: two 32x32x64 8-bit MFMAs (d 0..63 and
+//     64..127), Q^T held in registers, K row fragments from LDS;
+//   * online softmax in fp32 exactly as the bf16 forward; the probabilities
+//     are taken against the running maximum *times 2^8* (p' = 2^(s - m + 8),
+//     so 0 <= p' <= 256) and rounded to E4M3 -- the 8-bit format's largest
+//     value is 448 and its relative spacing 2^-3, so the rounding error is at
+//     most 2^-4 p' (2^-10 below 2^-6, the subnormal range); the running sum
+//     takes the unrounded p', so O = sum q(p') v / sum p' and the LSE is exact
+//     up to fp32 rounding;
+//   * O^T += V^T P^T per 64 keys and 32-wide d block: one 32x32x64 MFMA whose
+//     B operand packs the two score blocks' p' (C layout) and whose A operand
+//     comes from four 8-bit transposing LDS reads in the same key order;
+//   * epilogue: O = acc * v_descale / l (bf16), LSE = (m + log2 l - 8) ln 2.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kF8D = 128;       // head dim (bytes per 8-bit row)
+constexpr int kF8BC = 128;      // keys per tile
+constexpr int kF8NW = 8;        // waves per workgroup
+constexpr int kF8BR = kF8NW * 32;
+constexpr int kF8Tile = kF8BC * kF8D;           // bytes of one K or V tile
+constexpr int kF8Lds = 2 * 2 * kF8Tile;         // double-buffered K and V
+constexpr int kE8M0One = 127;                   // block scale exponent 0 (x1.0)
+
+// D = A B + C with 32x64 (A) and 64x32 (B) E4M3 operands, fp32 accumulate.
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8M0One, 0, kE8M0One);
+}
+
+__device__ __forceinline__ i32x8 join(i32x4 a, i32x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// K row fragment of MFMA m: this lane's row, bytes 64m + 32*(lane/32) .. +31.
+__device__ __forceinline__ i32x8 k_frag(const unsigned char* tile, int lane, int row0, int m) {
+  return join(*(const i32x4*)(tile + layout::f8_row_frag_off(lane, row0, m, 0)),
+              *(const i32x4*)(tile + layout::f8_row_frag_off(lane, row0, m, 1)));
+}
+
+// V^T fragment for d block db and the 64 keys k0 .. k0+63 (four transposing reads).
+__device__ __forceinline__ i32x8 vt_frag(const unsigned char* tile, int lane, int k0, int db) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  i32x2 r[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    r[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2*)(tile + layout::f8_tr_off(lane, k0, db, t)));
+  return i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+}
+
+// Four probabilities -> four E4M3 bytes (round to nearest even; 0 <= p <= 256).
+__device__ __forceinline__ int pack4_f8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+template <bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
+                          amdgpu_waves_per_eu(2, 2))) void attn_fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    const float* __restrict__ q_descale, const float* __restrict__ k_descale,
+    const float* __restrict__ v_descale, uint16_t* __restrict__ O, float* __restrict__ LSE,
+    int N, int BH, int Hq, int Hkv, int G, int n_qb, float tau_log2e, int xcd_remap) {
+  constexpr int KB = kF8BC / 32;   // 32-key score blocks per tile
+  constexpr int DB = kF8D / 32;    // 32-wide d blocks of O^T
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int bh, qrank;
+  const int w = blockIdx.x;
+  if (xcd_remap) {
+    const int hx = BH >> 3;
+    const int i = w >> 3;
+    bh = (w & 7) * hx + (i % hx);
+    qrank = i / hx;
+  } else {
+    bh = w % BH;
+    qrank = w / BH;
+  }
+  const int qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
+  const int b = bh / Hq, h = bh - b * Hq, hk = h / G;
+  const size_t kv_row0 = ((size_t)b * Hkv + hk) * N;
+  const uint8_t* Qp = Q + (size_t)bh * N * kF8D;
+  const uint8_t* Kp = K + kv_row0 * kF8D;
+  const uint8_t* Vp = V + kv_row0 * kF8D;
+  // scores in log2 units: tau * log2(e) * q_descale * k_descale
+  const float scale_log2 = tau_log2e * q_descale[bh] * k_descale[b * Hkv + hk];
+  const float vds = v_descale[b * Hkv + hk];
+
+  const int q0 = qb * kF8BR;
+  const int qw0 = q0 + wave * 32, qw1 = qw0 + 31;
+  const bool wave_live = qw0 < N;
+
+  // Q^T (B operand) of both MFMAs: this lane's query, bytes 64m + 32hi .. +31
+  i32x8 qf[2];
+  {
+    const int row = qw0 + l32;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t* src = Qp + (size_t)row * kF8D + 64 * m + 32 * hi;
+      qf[m] = row < N ? join(*(const i32x4*)src, *(const i32x4*)(src + 16)) : i32x8{};
+    }
+  }
+  // the Q loads' wait, once, before the tile loads start
+#pragma unroll
+  for (int m = 0; m < 2; ++m) asm volatile("" ::"v"(qf[m]));
+
+  const int kv_end = CAUSAL ? min(N, q0 + kF8BR) : N;
+  const int n_tiles = (kv_end + kF8BC - 1) / kF8BC;
+
+  // an 8-bit row of 128 bytes is loaded exactly like a d = 64 bf16 row
+  TileLoader<64, kF8BC, kF8NW> ldr;
+  ldr.init(wave, lane);
+  auto issue_tile = [&](int j, int buf) {
+    unsigned char* kt = smem + buf * 2 * kF8Tile;
+    ldr.load((const uint16_t*)Kp, j * kF8BC, N, kt, wave);
+    ldr.load((const uint16_t*)Vp, j * kF8BC, N, kt + kF8Tile, wave);
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  issue_tile(0, 0);
+  wait_all_memory();
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    const int kstart = j * kF8BC;
+    if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
+    if (wave_live && (!CAUSAL || kstart <= qw1)) {
+      const unsigned char* kt = smem + buf * 2 * kF8Tile;
+      const unsigned char* vt = kt + kF8Tile;
+
+      // S^T[x] = K_x Q^T: 32 keys x 32 queries, lane holds query column l%32
+      f32x16 s[KB];
+#pragma unroll
+      for (int x = 0; x < KB; ++x) {
+        s[x] = mfma_f8(k_frag(kt, lane, 32 * x, 0), qf[0], f32x16{});
+        s[x] = mfma_f8(k_frag(kt, lane, 32 * x, 1), qf[1], s[x]);
+      }
+
+      const bool need_mask = (kstart + kF8BC > N) || (CAUSAL && kstart + kF8BC - 1 > qw0);
+      if (need_mask) {
+        const int q = qw0 + l32;
+#pragma unroll
+        for (int x = 0; x < KB; ++x)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kstart + 32 * x + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (key >= N || (CAUSAL && key > q)) s[x][i] = -INFINITY;
+          }
+      }
+
+      // online softmax (exact running max; key 0 is visible to every row, so
+      // m_run is finite from the first visited tile on)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < KB; ++x)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[x][i]);
+      mx = pair_max(mx) * scale_log2;
+      const bool move = mx > m_run;
+      if (__any(move)) {
+        const float m_new = move ? mx : m_run;
+        const float alpha = exp2_fast(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      // p' = 2^(s - m + 8) in [0, 256]; the sum takes p' before rounding
+      const float shift = 8.f - m_run;
+      i32x8 pf[KB / 2];
+      float lsum = 0.f;
+#pragma unroll
+      for (int y = 0; y < KB / 2; ++y) {
+        int wv[8];
+#pragma unroll
+        for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              p[e] = exp2_fast(__builtin_fmaf(s[2 * y + xx][4 * r + e], scale_log2, shift));
+              lsum += p[e];
+            }
+            wv[4 * xx + r] = pack4_f8(p[0], p[1], p[2], p[3]);
+          }
+        pf[y] = i32x8{wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]};
+      }
+      l_run += lsum;
+
+      // O^T[db] += V^T P^T over the tile's two 64-key pairs
+#pragma unroll
+      for (int y = 0; y < KB / 2; ++y)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = mfma_f8(vt_frag(vt, lane, 64 * y, db), pf[y], acc[db]);
+    }
+    wait_all_memory();
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  const float lt = pair_sum(l_run);
+  const float inv = vds / lt;
+  const int q = qw0 + l32;
+  if (q < N) {
+    uint16_t* orow = O + ((size_t)bh * N + q) * kF8D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = db * 32 + 8 * r + 4 * hi;
+        const f32x16& a = acc[db];
+        *(u32x2*)(orow + d0) = u32x2{pack_bf16x2(a[4 * r + 0] * inv, a[4 * r + 1] * inv),
+                                     pack_bf16x2(a[4 * r + 2] * inv, a[4 * r + 3] * inv)};
+      }
+    if (hi == 0) LSE[(size_t)bh * N + q] = (m_run + log2_fast(lt) - 8.f) * kLn2;
+  }
+}
+
+template <bool CAUSAL>
+hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t stream) {
+  const int n_qb = (a.N + kF8BR - 1) / kF8BR;
+  const int BH = a.B * a.Hq;
+  const long long grid = (long long)BH * n_qb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  auto kern = attn_fwd_fp8_kernel<CAUSAL>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kF8NW * 64), kF8Lds, stream,
+                     (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_descale,
+                     a.k_descale, a.v_descale, (uint16_t*)a.o, a.lse, a.N, BH, a.Hq, a.Hkv,
+                     a.Hq / a.Hkv, n_qb, a.scale * kLog2e, xcd_remap(BH, Packing{}));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
+  return a.causal ? launch_fp8_t<true>(a, stream) : launch_fp8_t<false>(a, stream);
+}
+
+}  // namespace attn

@@ -63,6 +63,24 @@ inline size_t bwd_workspace_bytes(int B, int Hq, int N) {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
+// Forward over 8-bit (OCP E4M3) Q, K, V [B, H, N, d=128] with fp32 descales
+// [B, Hq] (q) and [B, Hkv] (k, v); O bf16, LSE fp32 as launch_fwd.
+struct Fp8FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, d;
+  bool causal;
+  float scale;
+};
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
+
 // Decoding against a KV cache: q [B, Hq, Nq, d], k/v [B, Hkv, Nk, d], Nq <= Nk,
 // queries at the last Nq positions.  Keys are split into n_splits chunks of
 // `chunk` keys (a multiple of 128); workspace holds the per-chunk partials.

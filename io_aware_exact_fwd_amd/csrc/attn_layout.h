@@ -80,5 +80,47 @@ ATTN_HD int tr_frag_off(int lane, int row0, int col0, int half) {
   return elem_off<D>(row, col);
 }
 
+// ---------------------------------------------------------------------------
+// 8-bit (E4M3) tiles, d = 128.  A row of 128 bytes is exactly a D = 64 bf16
+// row, and the tile uses that layout: 16-byte chunks, swz<64>, filled by the
+// same direct loads (direct_src<64>).  Its two access patterns are conflict
+// free as well:
+//   * row fragments of the 32x32x64 8-bit MFMA: lane l reads row row0 + l%32,
+//     bytes 64m + 32*(l/32) .. +31 (two chunks, two ds_read_b128);
+//   * transposed fragments (ds_read_b64_tr_b8; per group of 16 lanes, byte j
+//     of lane i is byte (i & 7) of the 8 bytes addressed by lane
+//     2j + (i >> 3)): a lane receives 8 keys of one d column per read.
+// ---------------------------------------------------------------------------
+
+// Byte offset of byte column `col` of row r in an 8-bit tile.
+ATTN_HD int f8_off(int r, int col) { return chunk_off<64>(r, col >> 4) + (col & 15); }
+
+// Row fragment, MFMA m (d bytes 64m .. 64m+63), half e of this lane's 32
+// bytes: the 16-byte read's offset.
+ATTN_HD int f8_row_frag_off(int lane, int row0, int m, int e) {
+  return chunk_off<64>(row0 + (lane & 31), 4 * m + 2 * (lane >> 5) + e);
+}
+
+// Key (relative to the 64-key pair) that byte b of a lane in lane-half hi
+// holds, in both operands of O^T += V^T P^T: bytes 16x + i come from
+// accumulator i of the score block x of the pair, whose C-layout row is
+// 8(i/4) + 4hi + (i%4).
+ATTN_HD int f8_pair_key(int hi, int b) {
+  const int x = b >> 4, i = b & 15;
+  return 32 * x + 8 * (i >> 2) + 4 * hi + (i & 3);
+}
+
+// Transposed fragment of V^T for d block db (columns 32db .. 32db+31) and the
+// 64 keys k0 .. k0+63, read t (bytes 8t .. 8t+7 of the lane's operand): the
+// address this lane supplies.  In each group of 16 lanes, lane 2j + s points
+// at the 8 bytes of row f8_pair_key(hi, 8t + j) starting at column
+// 32db + 16(g & 1) + 8s, so lane i of the group receives column
+// 32db + 16(g & 1) + i with byte j holding that key.
+ATTN_HD int f8_tr_off(int lane, int k0, int db, int t) {
+  const int g = lane >> 4, q = lane & 15, j = q >> 1, s = q & 1, hi = g >> 1;
+  const int row = k0 + f8_pair_key(hi, 8 * t + j);
+  return f8_off(row, 32 * db + 16 * (g & 1) + 8 * s);
+}
+
 }  // namespace layout
 }  // namespace attn

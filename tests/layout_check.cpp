@@ -4,7 +4,9 @@
 // gets exactly the elements the MFMA operand needs and (2) no access pattern
 // has LDS bank conflicts.  The transposed read is modelled from the measured
 // behaviour of ds_read_b64_tr_b16: in each group of 16 lanes, slot j of lane i
-// is element (i & 3) of the 4 values addressed by lane 4j + (i >> 2).
+// is element (i & 3) of the 4 values addressed by lane 4j + (i >> 2); and of
+// ds_read_b64_tr_b8 for the 8-bit tiles: byte j of lane i is byte (i & 7) of
+// the 8 bytes addressed by lane 2j + (i >> 3).
 #include <cstdio>
 #include <set>
 #include <vector>
@@ -79,7 +81,70 @@ void check(int rows) {
       }
 }
 
+// 8-bit tiles (d = 128 bytes per row): rows x 128 bytes.
+void check_f8(int rows) {
+  std::vector<int> lds(rows * 128, -1);   // one entry per byte; value = global row*128 + col
+  for (int b = 0; b < rows * 128; b += 16) {
+    int r, c;
+    direct_src<64>(b, r, c);
+    for (int e = 0; e < 16; ++e) lds[b + e] = r * 128 + c * 16 + e;
+  }
+  for (int r = 0; r < rows; ++r)
+    for (int col = 0; col < 128; ++col)
+      EXPECT(lds[f8_off(r, col)] == r * 128 + col, "f8_off(%d,%d)", r, col);
+  // row fragments: lane l gets row row0 + l%32, bytes 64m + 32(l/32) + 16e .. +15
+  for (int row0 = 0; row0 + 32 <= rows; row0 += 32)
+    for (int m = 0; m < 2; ++m)
+      for (int e = 0; e < 2; ++e) {
+        for (int lane = 0; lane < 64; ++lane) {
+          const int off = f8_row_frag_off(lane, row0, m, e);
+          EXPECT(off % 16 == 0, "f8 row frag misaligned");
+          for (int k = 0; k < 16; ++k)
+            EXPECT(lds[off + k] == (row0 + lane % 32) * 128 + 64 * m + 32 * (lane / 32) + 16 * e + k,
+                   "f8 row frag lane %d m %d e %d byte %d", lane, m, e, k);
+        }
+        for (int g = 0; g < 4; ++g) {
+          std::set<int> banks;
+          for (int lane = 16 * g; lane < 16 * g + 16; ++lane)
+            for (int w = 0; w < 4; ++w) banks.insert((f8_row_frag_off(lane, row0, m, e) / 4 + w) % 64);
+          EXPECT(banks.size() == 64, "f8 row frag bank conflict row0 %d m %d e %d group %d", row0, m, e, g);
+        }
+      }
+  // transposed fragments: lane l, byte 8t + j = V[k0 + key(hi, 8t + j)][32db + l%32]
+  for (int k0 = 0; k0 + 64 <= rows; k0 += 64)
+    for (int db = 0; db < 4; ++db)
+      for (int t = 0; t < 4; ++t) {
+        int addr[64];
+        for (int lane = 0; lane < 64; ++lane) {
+          addr[lane] = f8_tr_off(lane, k0, db, t);
+          EXPECT(addr[lane] % 8 == 0, "f8 tr misaligned");
+        }
+        for (int lane = 0; lane < 64; ++lane) {
+          const int g = lane >> 4, i = lane & 15, hi = lane >> 5;
+          for (int j = 0; j < 8; ++j) {
+            const int src = addr[16 * g + 2 * j + (i >> 3)] + (i & 7);
+            const int want = (k0 + f8_pair_key(hi, 8 * t + j)) * 128 + 32 * db + lane % 32;
+            EXPECT(lds[src] == want, "f8 tr k0 %d db %d t %d lane %d byte %d", k0, db, t, lane, j);
+          }
+        }
+        for (int half = 0; half < 2; ++half) {   // served 32 lanes (256 bytes) at a time
+          std::set<int> banks;
+          for (int lane = 32 * half; lane < 32 * half + 32; ++lane)
+            for (int w = 0; w < 2; ++w) banks.insert((addr[lane] / 4 + w) % 64);
+          EXPECT(banks.size() == 64, "f8 tr bank conflict k0 %d db %d t %d half %d (%zu banks)", k0, db, t,
+                 half, banks.size());
+        }
+      }
+  // the pair's keys: each lane-half sees every key of 64 exactly... once per
+  // pair of lane-halves: hi = 0 and hi = 1 together cover keys 0..63
+  std::set<int> keys;
+  for (int hi = 0; hi < 2; ++hi)
+    for (int b = 0; b < 32; ++b) keys.insert(f8_pair_key(hi, b));
+  EXPECT(keys.size() == 64 && *keys.begin() == 0 && *keys.rbegin() == 63, "f8 pair keys");
+}
+
 int main() {
+  check_f8(128);
   check<128>(64);
   check<128>(128);
   check<64>(64);

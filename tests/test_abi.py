@@ -24,7 +24,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
                                            "attn_bwd_window", "attn_bwd_grads_window",
                                            "attn_fwd_decode",
                                            "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
-                                           "attn_bwd_varlen", "attn_bwd_grads_varlen",
+                                           "attn_bwd_varlen", "attn_bwd_grads_varlen", "attn_fwd_fp8",
                                            "attn_bwd_varlen_workspace_bytes"])
 
 
@@ -219,3 +219,14 @@ def test_varlen_validation_and_workspace(L):
     assert g(*([A] * 9), None, 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 1
     assert g(*([A] * 10), 2, 100, 60, 4, 2, 64, 1, -1, -2.0, None) == 5
     assert g(*([A] * 5), MIS, *([A] * 4), 2, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 3
+
+
+def test_fp8_validation(L):
+    f = L.attn_fwd_fp8
+    #         q  k  v  qd kd vd o  lse B  Hq Hkv N   d   causal scale
+    assert f(A, A, A, A, A, A, A, A, 1, 4, 2, 64, 128, 1, 0.1, None) in (3, 6)   # valid: no device
+    assert f(A, A, A, A, A, A, A, A, 1, 4, 2, 64, 64, 1, 0.1, None) == 3         # d = 64: 8-bit path is d = 128
+    assert f(A, A, A, None, A, A, A, A, 1, 4, 2, 64, 128, 1, 0.1, None) == 1     # descale missing
+    assert f(A, A, A, A, A, A, A, A, 1, 4, 3, 64, 128, 1, 0.1, None) == 2        # Hq % Hkv
+    assert f(A, MIS, A, A, A, A, A, A, 1, 4, 2, 64, 128, 1, 0.1, None) == 3      # alignment
+    assert f(A, A, A, A, A, A, A, A, 1, 4, 2, 64, 128, 1, float("nan"), None) == 5
