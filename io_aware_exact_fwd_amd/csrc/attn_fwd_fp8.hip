@@ -41,7 +41,7 @@ constexpr int kF8BC = 128;      // keys per tile
 constexpr int kF8NW = 8;        // waves per workgroup
 constexpr int kF8BR = kF8NW * 32;
 constexpr int kF8Tile = kF8BC * kF8D;           // bytes of one K or V tile
-constexpr int kF8Lds = 2 * 2 * kF8Tile;         // double-buffered K and V
+constexpr int kF8Lds = 2 * 2 * kF8Tile;         // double-buffered K and V (64 KB)
 constexpr int kE8M0One = 127;                   // block scale exponent 0 (x1.0)
 
 // D = A B + C with 32x64 (A) and 64x32 (B) E4M3 operands, fp32 accumulate.
@@ -85,6 +85,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
     int N, int BH, int Hq, int Hkv, int G, int n_qb, float tau_log2e, int xcd_remap) {
   constexpr int KB = kF8BC / 32;   // 32-key score blocks per tile
   constexpr int DB = kF8D / 32;    // 32-wide d blocks of O^T
+  constexpr int kPrefK = 3;        // K fragments in flight ahead of their MFMA
+  constexpr int kPrefV = 2;        // V^T fragments in flight ahead of their MFMA
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
@@ -135,8 +137,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
   // an 8-bit row of 128 bytes is loaded exactly like a d = 64 bf16 row
   TileLoader<64, kF8BC, kF8NW> ldr;
   ldr.init(wave, lane);
-  auto issue_tile = [&](int j, int buf) {
-    unsigned char* kt = smem + buf * 2 * kF8Tile;
+  auto stage = [&](int j) { return smem + (j & 1) * 2 * kF8Tile; };
+  auto issue_tile = [&](int j) {
+    unsigned char* kt = stage(j);
     ldr.load((const uint16_t*)Kp, j * kF8BC, N, kt, wave);
     ldr.load((const uint16_t*)Vp, j * kF8BC, N, kt + kF8Tile, wave);
   };
@@ -146,24 +149,40 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  issue_tile(0, 0);
+  issue_tile(0);
   wait_all_memory();
   __syncthreads();
-
   for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
     const int kstart = j * kF8BC;
-    if (j + 1 < n_tiles) issue_tile(j + 1, buf ^ 1);
+    if (j + 1 < n_tiles) issue_tile(j + 1);
     if (wave_live && (!CAUSAL || kstart <= qw1)) {
-      const unsigned char* kt = smem + buf * 2 * kF8Tile;
+      const unsigned char* kt = stage(j);
       const unsigned char* vt = kt + kF8Tile;
 
-      // S^T[x] = K_x Q^T: 32 keys x 32 queries, lane holds query column l%32
+      // S^T[x] = K_x Q^T: 32 keys x 32 queries, lane holds query column l%32.
+      // Step i is key block i % KB, d half i / KB; the K fragments go through
+      // a ring of kPrefK registers, each read issued kPrefK MFMAs ahead.
       f32x16 s[KB];
 #pragma unroll
-      for (int x = 0; x < KB; ++x) {
-        s[x] = mfma_f8(k_frag(kt, lane, 32 * x, 0), qf[0], f32x16{});
-        s[x] = mfma_f8(k_frag(kt, lane, 32 * x, 1), qf[1], s[x]);
+      for (int x = 0; x < KB; ++x) s[x] = f32x16{};
+      {
+        constexpr int NS = 2 * KB;
+        i32x8 kr[kPrefK];
+#pragma unroll
+        for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(kt, lane, 32 * (i % KB), i / KB);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const i32x8 a = kr[i % kPrefK];
+          if (i + kPrefK < NS) kr[i % kPrefK] = k_frag(kt, lane, 32 * ((i + kPrefK) % KB), (i + kPrefK) / KB);
+          s[i % KB] = mfma_f8(a, qf[i / KB], s[i % KB]);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefK, 0);
+#pragma unroll
+        for (int i = 0; i < NS - kPrefK; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefK, 0);
       }
 
       const bool need_mask = (kstart + kF8BC > N) || (CAUSAL && kstart + kF8BC - 1 > qw0);
@@ -218,11 +237,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
       }
       l_run += lsum;
 
-      // O^T[db] += V^T P^T over the tile's two 64-key pairs
+      // O^T[db] += V^T P^T over the tile's two 64-key pairs; step i is pair
+      // i / DB, d block i % DB, with the V^T fragments kPrefV steps ahead
+      {
+        constexpr int NP = (KB / 2) * DB;
+        i32x8 vr[kPrefV];
 #pragma unroll
-      for (int y = 0; y < KB / 2; ++y)
+        for (int i = 0; i < kPrefV; ++i) vr[i] = vt_frag(vt, lane, 64 * (i / DB), i % DB);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] = mfma_f8(vt_frag(vt, lane, 64 * y, db), pf[y], acc[db]);
+        for (int i = 0; i < NP; ++i) {
+          const i32x8 a = vr[i % kPrefV];
+          if (i + kPrefV < NP) vr[i % kPrefV] = vt_frag(vt, lane, 64 * ((i + kPrefV) / DB), (i + kPrefV) % DB);
+          acc[i % DB] = mfma_f8(a, pf[i / DB], acc[i % DB]);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPrefV, 0);
+#pragma unroll
+        for (int i = 0; i < NP - kPrefV; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefV, 0);
+      }
     }
     wait_all_memory();
     __syncthreads();
