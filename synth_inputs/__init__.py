@@ -23,6 +23,12 @@ is cut to fit).
 ``descale = max|x| / 448`` (fp32) and ``code = E4M3(x / descale)``, rounded to
 the nearest representable value, ties to even (``f32_to_e4m3_bits``).
 
+Very large inputs (tensors of several GiB, drawn where they are used) come
+from ``hashed_bf16_bits``: element i of a stream with seed s is the SplitMix64
+output for state s + (i + 1) * 0x9E3779B97F4A7C15, whose low 16 bits give a
+sign, a power of two in [1/8, 1] and 7 mantissa bits.  It uses integer
+operations only, so a GPU and the CPU produce the same bits for any slice.
+
 The bf16 payload is returned as ``uint16`` bit patterns; ``bf16_bits_to_f32``
 and ``bf16_bits_to_f64`` decode them exactly.
 """
@@ -47,6 +53,8 @@ __all__ = [
     "cu_from_lengths",
     "f32_to_e4m3_bits",
     "make_fp8_inputs",
+    "hashed_bf16_bits",
+    "splitmix64_reference",
 ]
 
 
@@ -186,6 +194,54 @@ def make_fp8_inputs(B: int, Hq: int, Hkv: int, N: int, d: int, seed: int) -> Dic
         descale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
         out[name + "8"] = f32_to_e4m3_bits(f.astype(np.float64) / descale.astype(np.float64)[:, :, None, None])
         out[name + "_descale"] = descale
+    return out
+
+
+_GOLDEN = 0x9E3779B97F4A7C15
+_MIX1 = 0xBF58476D1CE4E5B9
+_MIX2 = 0x94D049BB133111EB
+_M64 = (1 << 64) - 1
+
+
+def splitmix64_reference(seed: int, i: int) -> int:
+    """SplitMix64 output number i (0-based) of a generator seeded with `seed`,
+    in plain Python integers (the published definition)."""
+    z = (seed + (i + 1) * _GOLDEN) & _M64
+    z = ((z ^ (z >> 30)) * _MIX1) & _M64
+    z = ((z ^ (z >> 27)) * _MIX2) & _M64
+    return z ^ (z >> 31)
+
+
+def _signed(c: int) -> int:
+    return c - (1 << 64) if c >= (1 << 63) else c
+
+
+def _lsr(z, s: int):
+    """Logical right shift of int64 tensors (torch's >> is arithmetic)."""
+    return (z >> s) & ((1 << (64 - s)) - 1)
+
+
+def hashed_bf16_bits(start: int, count: int, seed: int, device="cpu", chunk: int = 1 << 26):
+    """bf16 bit patterns (torch.int16) of stream elements start .. start+count-1.
+
+    Low 16 bits h of the SplitMix64 output: sign = bit 15, exponent field
+    124 + bits 7..8 (a power of two in [1/8, 1]), mantissa = bits 0..6.
+    int64 arithmetic wraps identically on every device.
+    """
+    import torch
+    out = torch.empty(count, dtype=torch.int16, device=device)
+    g, m1, m2 = _signed(_GOLDEN), _signed(_MIX1), _signed(_MIX2)
+    for c0 in range(0, count, chunk):
+        n = min(chunk, count - c0)
+        i = torch.arange(start + c0, start + c0 + n, dtype=torch.int64, device=device)
+        z = (i + 1) * g + _signed(seed & _M64)
+        z = (z ^ _lsr(z, 30)) * m1
+        z = (z ^ _lsr(z, 27)) * m2
+        z = z ^ _lsr(z, 31)
+        h = z & 0xFFFF
+        bits = ((h >> 15) << 15) | ((124 + ((h >> 7) & 3)) << 7) | (h & 0x7F)
+        out[c0:c0 + n] = (bits - ((bits >> 15) << 16)).to(torch.int16)   # as signed 16-bit
+        del i, z, h, bits
     return out
 
 

@@ -102,3 +102,22 @@ def test_packed_workload_inputs():
     for name in ("q", "k", "v", "do"):
         assert (p[name] == y[name][0]).all()
     assert p["cu_seqlens"].tolist()[-1] == 64 and len(p["cu_seqlens"]) == len(small.lengths()) + 1
+
+
+def test_hashed_stream_follows_splitmix64():
+    """The integer-only large-input stream equals the published SplitMix64 on
+    plain Python integers, and its bits decode to the stated values."""
+    import torch
+    from synth_inputs import hashed_bf16_bits, splitmix64_reference
+    assert splitmix64_reference(0, 0) == 0xE220A8397B1DCDAF      # first output, seed 0
+    for seed in (0, 12345, 2 ** 63 + 7):
+        got = hashed_bf16_bits(1000, 300, seed, chunk=128).view(torch.uint16).to(torch.int64).tolist()
+        for k, g in enumerate(got):
+            h = splitmix64_reference(seed, 1000 + k) & 0xFFFF
+            assert g == ((h >> 15) << 15) | ((124 + ((h >> 7) & 3)) << 7) | (h & 0x7F)
+    v = bf16_bits_to_f32(hashed_bf16_bits(0, 4096, 3).view(torch.uint16).numpy())
+    a = np.abs(v)
+    assert (a >= 0.125).all() and (a < 2.0).all() and (v < 0).any() and (v > 0).any()
+    # a slice of the stream is the same stream
+    full = hashed_bf16_bits(0, 5000, 9, chunk=777)
+    assert torch.equal(full[1234:2345], hashed_bf16_bits(1234, 1111, 9))
