@@ -258,8 +258,8 @@ int attn_bwd_grads_varlen(const void* q, const void* k, const void* v, const voi
  * scaling by 2^8 (relative error <= 2^-4, absolute <= 2^-18 of the row's
  * largest probability in the subnormal range), so |O - O_exact| <=
  * sum_j max(2^-4 P_ij, 2^-18 max_k P_ik) |v_j| plus O's own bf16 rounding.
- * NaN codes give NaN rows.  Errors as attn_fwd, with ATTN_ERR_UNSUPPORTED for
- * d != 128.
+ * A NaN code is not an error: it propagates into the outputs of the rows that
+ * read it.  Errors as attn_fwd, with ATTN_ERR_UNSUPPORTED for d != 128.
  */
 int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                  const float* k_descale, const float* v_descale, void* o, float* lse,

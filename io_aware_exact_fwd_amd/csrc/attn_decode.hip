@@ -322,7 +322,8 @@ int decode_splits(int B, int Hq, int Hkv, int Nq, int Nk, int requested, int* ch
   const int n_tiles = (Nk + kDecBC - 1) / kDecBC;
   int s = requested;
   if (s <= 0) {
-    // enough workgroups for two per CU on 256 CUs, at least one tile each
+    // about two rounds of workgroups over the 256 CUs (one resident per CU:
+    // 128 KB of LDS), at least one tile each
     const long long base = (long long)B * Hkv * n_rb;
     s = (int)((512 + base - 1) / base);
   }
