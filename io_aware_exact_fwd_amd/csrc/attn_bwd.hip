@@ -522,9 +522,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                                        scale_log2, xcd_q, window, pk, w - n_dkdv, smem);
 }
 
+// Dynamic LDS beyond 64 KB, allowed once per kernel instance and device.
 template <typename KernelT>
-hipError_t allow_lds(KernelT kern, int bytes) {
-  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+hipError_t allow_lds(KernelT kern, int bytes, std::atomic<uint64_t>& done) {
+  return allow_lds_on_device((const void*)kern, bytes, done);
 }
 
 template <int D>
@@ -546,7 +547,8 @@ struct LaunchDkdv {
   static hipError_t run(const BwdArgs& a, hipStream_t stream) {
     using CK = DkdvCfg<D, kDkdvNWK>;
     auto kern = bwd_dkdv_kernel<D, kDkdvNWK, kDkdvWPE, CAUSAL, LOCAL>;
-    static const hipError_t attr = allow_lds(kern, CK::kLdsBytes);
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t attr = allow_lds(kern, CK::kLdsBytes, lds_set);
     if (attr != hipSuccess) return attr;
     const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
     const int BHkv = a.B * a.Hkv;
@@ -566,7 +568,8 @@ struct LaunchDq {
   static hipError_t run(const BwdArgs& a, hipStream_t stream) {
     using CQ = DqCfg<D, kDqBC, kDqNW>;
     auto kern = bwd_dq_kernel<D, kDqBC, kDqNW, kDqWPE, CAUSAL, LOCAL>;
-    static const hipError_t attr = allow_lds(kern, CQ::kLdsBytes);
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t attr = allow_lds(kern, CQ::kLdsBytes, lds_set);
     if (attr != hipSuccess) return attr;
     const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
     const int BH = a.B * a.Hq;
@@ -589,7 +592,8 @@ struct LaunchGrads {
     static_assert(CK::kThreads == CQ::kThreads, "one workgroup size for both halves");
     constexpr int lds = CK::kLdsBytes > CQ::kLdsBytes ? CK::kLdsBytes : CQ::kLdsBytes;
     auto kern = bwd_grads_kernel<D, kDkdvNWK, kDqBC, kDqNW, kDqWPE, CAUSAL, LOCAL>;
-    static const hipError_t attr = allow_lds(kern, lds);
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t attr = allow_lds(kern, lds, lds_set);
     if (attr != hipSuccess) return attr;
     const int BHkv = a.B * a.Hkv, BH = a.B * a.Hq;
     const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;

@@ -298,8 +298,8 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   const long long grid = (long long)n_bhk * n_rb * a.n_splits;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto kern = attn_decode_split_kernel<D, CAUSAL, LOCAL>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t attr = allow_lds_on_device((const void*)kern, C::kLdsBytes, lds_set);
   if (attr != hipSuccess) return attr;
   float* o_part = a.workspace;
   float* lse_part = o_part + (size_t)a.n_splits * rows_total * D;

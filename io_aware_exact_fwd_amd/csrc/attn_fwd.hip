@@ -282,9 +282,9 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)BH * n_qb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto kern = attn_fwd_kernel<D, BC, NW, WPE, CAUSAL, LOCAL, LAG>;
-  // more than 64 KB of dynamic LDS has to be allowed once per kernel instance
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  // more than 64 KB of dynamic LDS has to be allowed per kernel instance and device
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t attr = allow_lds_on_device((const void*)kern, C::kLdsBytes, lds_set);
   if (attr != hipSuccess) return attr;
   const int remap = xcd_remap(BH, a.pack);
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, stream,

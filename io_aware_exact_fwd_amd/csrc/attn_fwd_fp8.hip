@@ -289,8 +289,8 @@ hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t stream) {
   const long long grid = (long long)BH * n_qb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   auto kern = attn_fwd_fp8_kernel<CAUSAL>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kF8Lds);
+  static std::atomic<uint64_t> lds_set{0};
+  const hipError_t attr = allow_lds_on_device((const void*)kern, kF8Lds, lds_set);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kF8NW * 64), kF8Lds, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_descale,

@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+#include <cstdint>
+
 namespace attn {
 
 // Packed variable-length batches: tensors are [H, T, d] with the B sequences
@@ -14,6 +17,20 @@ struct Packing {
   const int* cu = nullptr;  // B + 1 boundaries, device memory
   int T = 0;                // packed rows per head
 };
+
+// Allows `bytes` of dynamic LDS (more than the default 64 KB) for `kern` on
+// the current device.  The attribute is set once per device; `done` is the
+// caller's per-kernel mask of devices already set (devices 0..63).
+inline hipError_t allow_lds_on_device(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Whether a grid over `units` (batch, head) pairs keeps all blocks of a pair
 // on one XCD (workgroup w runs on XCD w % 8).  That keeps a pair's K/V tiles in
