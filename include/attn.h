@@ -28,8 +28,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are dense, contiguous, row-major [B, H, N, d] (batch, heads,
- *    sequence, head dim) -- the "(Batch, Heads, Seq_Len, Dim)" layout of
- *    [EVOL] §6.  Q, O, dO, dQ have H = Hq heads; K, V, dK, dV have H = Hkv.
+ *    sequence, head dim), the tensor layout of the example in [EVOL] §6.
+ *    Q, O, dO, dQ have H = Hq heads; K, V, dK, dV have H = Hkv.
  *  - bf16 tensors hold IEEE-style bfloat16 bit patterns (uint16 storage).
  *    The log-sum-exp and the backward's workspace are fp32.
  *  - Grouped heads: query head h reads K/V head h / (Hq / Hkv); Hkv = 1 is
