@@ -154,9 +154,35 @@ def parse():
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/counters.json from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--ingest-mfma", metavar="MFMA_CSV", default=None)
+    ap.add_argument("--cold-cache", choices=("auto", "on", "off"), default="auto",
+                    help="also time each kernel after a 512 MiB scratch write that flushes L2 and "
+                         "the last-level cache (auto: fwd-2K only)")
     ap.add_argument("--cpu-sample-heads", type=int, default=None,
                     help="query heads in the oracle's timed sample (default: sized for ~10-30 s)")
     return ap.parse_args()
+
+
+def host_info() -> dict:
+    """What the CPU baseline ran on: model, usable cores, thread settings, BLAS build."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import numpy as np
+    import torch
+    blas = None
+    try:
+        deps = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{deps.get('name')} {deps.get('version')}"
+    except Exception:  # older numpy: no dict mode
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
+            "torch_threads": torch.get_num_threads(), "numpy_blas": blas}
 
 
 def cpu_baseline(w, x, n_heads):
@@ -185,7 +211,7 @@ def cpu_baseline(w, x, n_heads):
             "sample": f"fp64 oracle forward of the dequantized E4M3 inputs on query heads 0..{hq - 1} "
                       f"of {w.Hq}, full N={w.N}, same seeded inputs (algorithmic {flops:.3g} FLOP in "
                       f"{dt:.2f} s; the oracle evaluates full masked rows)",
-            "host": platform.processor() or platform.machine(),
+            "host": host_info(),
         }
     if w.pack is not None:
         # packed batch: every sequence of the first hq query heads
@@ -202,7 +228,7 @@ def cpu_baseline(w, x, n_heads):
             "sample": f"fp64 oracle {what} on query heads 0..{hq - 1} of {w.Hq}, every packed "
                       f"sequence ({len(cu) - 1}, T={w.N}), same seeded inputs (algorithmic "
                       f"{flops:.3g} FLOP in {dt:.2f} s; the oracle evaluates full masked rows)",
-            "host": platform.processor() or platform.machine(),
+            "host": host_info(),
         }
     sl = lambda name, h: torch.from_numpy(bf16_bits_to_f64(x[name][:nb, :h].copy()))
     q, k, v = sl("q", hq), sl("k", hk), sl("v", hk)
@@ -219,7 +245,7 @@ def cpu_baseline(w, x, n_heads):
         "sample": f"fp64 oracle {what} on batches 0..{nb - 1}, query heads 0..{hq - 1} of {w.Hq}, full N={w.N}, "
                   f"same seeded inputs (algorithmic {flops:.3g} FLOP in {dt:.2f} s; the oracle "
                   f"evaluates full masked rows)",
-        "host": platform.processor() or platform.machine(),
+        "host": host_info(),
     }
 
 
@@ -252,8 +278,8 @@ def main():
         sys.exit(1)
 
     w = WORKLOADS[args.workload]
-    steps = args.steps if args.steps is not None else (20 if w.with_grad else 50)
-    warmup = args.warmup if args.warmup is not None else 3
+    steps = args.steps if args.steps is not None else 50
+    warmup = args.warmup if args.warmup is not None else 10
     x = make_inputs(w)
 
     def dev(bits):
@@ -341,6 +367,20 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_per_step = wall * 1e3 / steps
+
+    # cold-cache leg (untimed in ``value``): before each step a 512 MiB scratch
+    # write evicts L2 and the last-level cache, so the inputs come from HBM again
+    cold = args.cold_cache == "on" or (args.cold_cache == "auto" and w.name == "fwd-2K")
+    cold_events = []
+    if cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+                       for _ in range(steps)]
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            step(cold_events[i])
+        torch.cuda.synchronize()
+        del scratch
     pairs = w.pairs(True)
     # algorithmic matmul FLOPs per unmasked pair, by kernel: the forward's QK^T
     # and PV (4d); the gradient kernel's S, dP, dV, dK and dQ (10d -- the dQ
@@ -355,14 +395,22 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     mfma_peak = PEAK_FP8_TFLOPS if w.fp8 else PEAK_BF16_TFLOPS
+    def stats(ms):
+        return {"ms_avg": float(np.mean(ms)), "ms_median": float(np.median(ms)), "ms_min": float(np.min(ms)),
+                "ms_p90": float(np.percentile(ms, 90))}
+
     parts = {}
     for i, ph in enumerate(phases):
-        ms = [e[i].elapsed_time(e[i + 1]) for e in events]
-        avg = float(np.mean(ms))
+        st = stats([e[i].elapsed_time(e[i + 1]) for e in events])
         flops = per_pair[ph] * pairs
-        parts[ph] = {"kernel": kernel_name[ph], "ms_avg": avg, "ms_median": float(np.median(ms)),
-                     "algorithmic_flops": flops, "tflops": flops / (avg * 1e-3) / 1e12}
+        parts[ph] = {"kernel": kernel_name[ph], **st, "algorithmic_flops": flops,
+                     "tflops": flops / (st["ms_avg"] * 1e-3) / 1e12,
+                     "tflops_median": flops / (st["ms_median"] * 1e-3) / 1e12}
         parts[ph]["pct_of_peak"] = 100 * parts[ph]["tflops"] / mfma_peak
+        if cold_events:
+            cs = stats([e[i].elapsed_time(e[i + 1]) for e in cold_events])
+            cs["tflops_median"] = flops / (cs["ms_median"] * 1e-3) / 1e12
+            parts[ph]["cold_cache"] = cs
     if w.with_grad:
         bwd_ms = sum(parts[p]["ms_avg"] for p in phases[1:])
         parts["bwd_total"] = {"ms_avg": bwd_ms, "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
@@ -408,6 +456,8 @@ def main():
         "pct_of_peak": 100 * value / mfma_peak,
         "parts": parts,
         "roofline": roofline,
+        "versions": {"torch": torch.__version__, "hip": torch.version.hip,
+                     "arch": torch.cuda.get_device_properties(0).gcnArchName},
     }
     if not args.no_cpu_baseline:
         default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1,

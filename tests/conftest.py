@@ -1,3 +1,4 @@
+import json
 import os
 import sys
 
@@ -29,3 +30,26 @@ def gpu_lib():
     rc = attn.device_check(torch.cuda.current_device())
     assert rc == 0, attn.strerror(rc)
     return attn
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Worst logged errors per test file (logged, not gated; see gpu_helpers)."""
+    mod = sys.modules.get("gpu_helpers")
+    log = getattr(mod, "ERROR_LOG", None) if mod else None
+    if not log:
+        return
+    path = os.environ.get("ATTN_PARITY_LOG")
+    if path:
+        with open(path, "w") as f:
+            for r in log:
+                f.write(json.dumps(r) + "\n")
+    tr = terminalreporter
+    tr.section("parity errors (worst per file; abs = absolute, rel = / max|ref|)")
+    tr.write_line(f"{'file':<24}{'kind':<5}{'n':>6}{'max':>11}{'mean':>11}{'vs rounded':>12}{'floor':>11}")
+    groups = {}
+    for r in log:
+        groups.setdefault((r["test"].split("::")[0].split("/")[-1], r["kind"]), []).append(r)
+    for (f, kind), rs in sorted(groups.items()):
+        tr.write_line(f"{f:<24}{kind:<5}{len(rs):>6}" + "".join(
+            f"{max(r[c] for r in rs):>{w}.3e}" for c, w in
+            (("max", 11), ("mean", 11), ("max_vs_rounded_oracle", 12), ("rounding_floor", 11))))

@@ -1,4 +1,13 @@
-"""Helpers shared by the GPU parity tests (no attention arithmetic here)."""
+"""Helpers shared by the GPU parity tests (no attention arithmetic here).
+
+Every comparison made through ``max_abs`` or ``rel_maxnorm`` is also logged,
+not gated: the mean error, the error against the oracle rounded to the
+output's storage type (bf16 for O and the gradients, fp32 for LSE), and that
+rounding's own size, the floor no kernel can go below.  ``conftest`` prints
+the worst of them per test file at the end of the session and, when
+``ATTN_PARITY_LOG`` names a file, writes every record there as JSON lines.
+"""
+import os
 import sys
 
 import numpy as np
@@ -32,7 +41,32 @@ def dev_f64(t: torch.Tensor) -> torch.Tensor:
     return t.detach().float().cpu().double()
 
 
+ERROR_LOG: list = []
+
+
+def _storage_round(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """b rounded to a's storage type: bf16 if every value of a is a bf16 value, else fp32."""
+    if a.numel() and bool((a.to(torch.bfloat16).double() == a).all()):
+        return b.to(torch.bfloat16).double()
+    return b.float().double()
+
+
+def _log(kind: str, a: torch.Tensor, b: torch.Tensor, scale: float) -> None:
+    if a.numel() == 0:
+        return
+    diff = (a - b).abs()
+    rb = _storage_round(a, b)
+    ERROR_LOG.append({
+        "test": os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0],
+        "kind": kind, "n": a.numel(),
+        "max": float(diff.max()) / scale, "mean": float(diff.mean()) / scale,
+        "max_vs_rounded_oracle": float((a - rb).abs().max()) / scale,
+        "rounding_floor": float((rb - b).abs().max()) / scale,
+    })
+
+
 def max_abs(a: torch.Tensor, b: torch.Tensor) -> float:
+    _log("abs", a, b, 1.0)
     return float((a - b).abs().max())
 
 
@@ -44,4 +78,6 @@ def rel_maxnorm(a: torch.Tensor, b: torch.Tensor, floor: float = 0.0) -> float:
     gradient of the same problem -- keeps the ratio meaningful there and is
     far below max |b| in every other case.
     """
-    return float((a - b).abs().max() / max(float(b.abs().max()), floor, 1e-30))
+    den = max(float(b.abs().max()), floor, 1e-30)
+    _log("rel", a, b, den)
+    return float((a - b).abs().max() / den)
