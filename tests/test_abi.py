@@ -230,3 +230,22 @@ def test_fp8_validation(L):
     assert f(A, A, A, A, A, A, A, A, 1, 4, 3, 64, 128, 1, 0.1, None) == 2        # Hq % Hkv
     assert f(A, MIS, A, A, A, A, A, A, 1, 4, 2, 64, 128, 1, 0.1, None) == 3      # alignment
     assert f(A, A, A, A, A, A, A, A, 1, 4, 2, 64, 128, 1, float("nan"), None) == 5
+
+
+def test_library_imports_no_allocation_or_copy():
+    """The library's only device work is kernel launches: it imports no
+    allocator and no copy or fill routine (host or device), so every buffer is
+    the caller's and no call hides an allocation or a transfer."""
+    import shutil
+    import subprocess
+
+    import io_aware_exact_fwd_amd as attn
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", attn.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    names = [line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()]
+    assert "hipLaunchKernel" in names
+    bad = [n for n in names if re.search(r"(?i)alloc|free|memcpy|memset|hostregister|mmap", n)]
+    assert bad == [], bad
