@@ -22,7 +22,7 @@ import torch  # loads the HIP runtime that libattn.so then binds to
 __all__ = [
     "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads", "fwd_decode",
     "decode_workspace_bytes", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
-    "bwd_grads_varlen", "fwd_fp8",
+    "bwd_grads_varlen", "fwd_fp8", "attention", "attention_varlen",
     "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
 ]
@@ -482,3 +482,63 @@ def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_descale: tor
     if rc != ATTN_OK:
         raise AttnError(rc, "attn_fwd_fp8")
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Autograd entry points: the forward keeps O and the LSE for the backward,
+# which recomputes the scores from them (nothing N x N is saved).  Both calls
+# only route tensors to the functions above.
+# ---------------------------------------------------------------------------
+class _Attention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale, window):
+        o, lse = fwd(q, k, v, causal=causal, scale=scale, window=window)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (causal, scale, window)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        causal, scale, window = ctx.args
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), causal=causal, scale=scale, window=window)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+              scale: Optional[float] = None, window: Optional[int] = None,
+              return_lse: bool = False):
+    """Differentiable attention on [B, H, N, d] bf16 CUDA tensors (H_q a multiple
+    of H_kv).  Returns O, or (O, LSE) with ``return_lse``; gradients reach q, k
+    and v through attn_bwd (or attn_bwd_window)."""
+    o, lse = _Attention.apply(q, k, v, bool(causal), scale, window)
+    return (o, lse) if return_lse else o
+
+
+class _AttentionVarlen(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cu_seqlens, max_seqlen, causal, scale, window):
+        o, lse = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=causal, scale=scale, window=window)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.args = (cu_seqlens, max_seqlen, causal, scale, window)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        cu_seqlens, max_seqlen, causal, scale, window = ctx.args
+        dq, dk, dv = bwd_varlen(q, k, v, o, lse, do.contiguous(), cu_seqlens, max_seqlen,
+                                causal=causal, scale=scale, window=window)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def attention_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
+                     max_seqlen: Optional[int] = None, causal: bool = True,
+                     scale: Optional[float] = None, window: Optional[int] = None,
+                     return_lse: bool = False):
+    """Differentiable attention over a packed batch: q [Hq, T, d], k/v [Hkv, T, d]
+    bf16, sequences at cu_seqlens (as for fwd_varlen).  Returns O, or (O, LSE)."""
+    o, lse = _AttentionVarlen.apply(q, k, v, cu_seqlens, max_seqlen, bool(causal), scale, window)
+    return (o, lse) if return_lse else o

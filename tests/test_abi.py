@@ -249,3 +249,15 @@ def test_library_imports_no_allocation_or_copy():
     assert "hipLaunchKernel" in names
     bad = [n for n in names if re.search(r"(?i)alloc|free|memcpy|memset|hostregister|mmap", n)]
     assert bad == [], bad
+
+
+def test_autograd_entry_points_reject_host_tensors():
+    """The differentiable wrappers validate like the direct calls: host tensors
+    are refused before anything reaches the library."""
+    import io_aware_exact_fwd_amd as attn
+    q = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attention(q, q, q)
+    qp = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attention_varlen(qp, qp, qp, [0, 3, 8], 5)
