@@ -22,6 +22,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import platform
 import sys
@@ -354,9 +355,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    # Without --warmup, warm up for at least 10 steps and 1 s, so that short
+    # workloads run at the clock a sustained job sees; without --steps, time at
+    # least 50 steps and at least 1 s.  Explicit values are used as given.
+    min_seconds = 1.0
+    if args.warmup is not None:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+    else:
+        warmup = 0
+        t_w = time.perf_counter()
+        while True:
+            for _ in range(10):
+                step()
+            warmup += 10
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_w >= min_seconds:
+                break
+        if args.steps is None:
+            per_step = (time.perf_counter() - t_w) / warmup
+            steps = max(steps, min(20000, math.ceil(min_seconds / per_step)))
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
@@ -374,9 +393,10 @@ def main():
     cold_events = []
     if cold:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold_steps = min(steps, 200)
         cold_events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
-                       for _ in range(steps)]
-        for i in range(steps):
+                       for _ in range(cold_steps)]
+        for i in range(cold_steps):
             scratch.fill_(i & 0xFF)
             step(cold_events[i])
         torch.cuda.synchronize()
