@@ -3,7 +3,8 @@
 Each case draws B, H_q, H_kv (a divisor), N (ragged, 1..700), d, the causal
 flag, an optional window and an optional scale from a fixed seed, then checks
 the forward and backward (fixed-length and windowed), the decode forward
-(N_q < N_k) and the packed variable-length calls at the usual bars.  The
+(N_q < N_k) and the packed variable-length calls at the usual bars, and the
+8-bit forward (d = 128, no window) at its per-element rounding bound.  The
 cases are small, so every element is compared.
 """
 import numpy as np
@@ -12,7 +13,8 @@ import torch
 
 from gpu_helpers import TOL_GRAD_REL, TOL_LSE, TOL_O, dev_f64, max_abs, rel_maxnorm, say, to_dev, to_f64
 from oracle import attention_backward, attention_forward, varlen_backward, varlen_forward
-from synth_inputs import cu_from_lengths, make_custom_inputs
+from synth_inputs import cu_from_lengths, make_custom_inputs, make_fp8_inputs
+from test_gpu_fp8 import check as check_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +95,12 @@ def test_random_packed(gpu_lib, i):
     eo, el, eg = max_abs(dev_f64(o), ro), max_abs(dev_f64(lse), rl), grads_err(g, rg)
     print(f"O={eo:.3g} LSE={el:.3g} grads={eg:.3g}")
     assert eo <= TOL_O and el <= TOL_LSE and eg <= TOL_GRAD_REL
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_fp8(gpu_lib, i):
+    c = draw_case(300 + i)
+    say(f"random 8-bit case {i}: B={c['B']} Hq={c['Hq']} Hkv={c['Hkv']} N={c['N']} causal={c['causal']} "
+        f"scale={c['scale']}")
+    x = make_fp8_inputs(c["B"], c["Hq"], c["Hkv"], c["N"], 128, seed=c["seed"])
+    check_fp8(gpu_lib, x, c["causal"], c["scale"], label=f"random fp8 {i}")
