@@ -160,6 +160,9 @@ def parse():
                          "the last-level cache (auto: fwd-2K only)")
     ap.add_argument("--cpu-sample-heads", type=int, default=None,
                     help="query heads in the oracle's timed sample (default: sized for ~10-30 s)")
+    ap.add_argument("--forward-legs", choices=("auto", "on", "off"), default="auto",
+                    help="also time the forward alone at fwd-8K and gqa-16K, reported under "
+                         "parts.fwd8k / parts.gqa16k (auto: with the default fb-32K workload)")
     return ap.parse_args()
 
 
@@ -248,6 +251,66 @@ def cpu_baseline(w, x, n_heads):
                   f"evaluates full masked rows)",
         "host": host_info(),
     }
+
+
+# Secondary forward-only legs: the north-star's own forward configurations,
+# timed after the headline step with the same warm-up and timing rules; they
+# do not enter ``value``.
+FORWARD_LEGS = (("fwd8k", "fwd-8K"), ("gqa16k", "gqa-16K"))
+
+
+def time_forward_leg(attn, name, steps_arg, warmup_arg, min_seconds=1.0):
+    """Mean/median/min/p90 of attn_fwd at one workload (inputs resident in HBM,
+    each launch bracketed by events on the stream it runs on)."""
+    import numpy as np
+    import torch
+
+    from synth_inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[name]
+    x = make_inputs(w)
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    del x
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    launch = lambda: attn.fwd(q, k, v, causal=True, out=o, lse=lse, stream=stream)
+    t_w = time.perf_counter()
+    if warmup_arg is not None:
+        warmup = warmup_arg
+        for _ in range(warmup):
+            launch()
+        torch.cuda.synchronize()
+    else:
+        warmup = 0
+        while True:
+            for _ in range(10):
+                launch()
+            warmup += 10
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_w >= min_seconds:
+                break
+    per_launch = (time.perf_counter() - t_w) / max(warmup, 1)
+    steps = steps_arg if steps_arg is not None else max(50, min(20000, math.ceil(min_seconds / per_launch)))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    flops = w.fwd_flops(True)
+    leg = {"workload": name, "kernel": "attn_fwd_kernel", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N,
+           "d": w.d, "causal": True, "input_scale": w.in_scale, "seed": w.seed, "warmup": warmup,
+           "steps": steps, "ms_avg": float(np.mean(ms)), "ms_median": float(np.median(ms)),
+           "ms_min": float(np.min(ms)), "ms_p90": float(np.percentile(ms, 90)), "algorithmic_flops": flops}
+    leg["tflops"] = flops / (leg["ms_avg"] * 1e-3) / 1e12
+    leg["tflops_median"] = flops / (leg["ms_median"] * 1e-3) / 1e12
+    leg["pct_of_peak"] = 100 * leg["tflops"] / PEAK_BF16_TFLOPS
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return leg
 
 
 def main():
@@ -479,6 +542,10 @@ def main():
         "versions": {"torch": torch.__version__, "hip": torch.version.hip,
                      "arch": torch.cuda.get_device_properties(0).gcnArchName},
     }
+    legs = args.forward_legs == "on" or (args.forward_legs == "auto" and w.name == "fb-32K")
+    if legs:
+        for key, name in FORWARD_LEGS:
+            parts[key] = time_forward_leg(attn, name, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         default_heads = {"fb-32K": 1, "gqa-16K": 8, "fwd-8K": 16, "fwd-2K": 64, "swa-32K": 1,
                          "decode-32K": 32, "varlen-32K": 3, "fp8-8K": 16}[w.name]

@@ -259,14 +259,23 @@ int attn_bwd_grads_varlen(const void* q, const void* k, const void* v, const voi
  * largest probability in the subnormal range), so |O - O_exact| <=
  * sum_j max(2^-4 P_ij, 2^-18 max_k P_ik) |v_j| plus O's own bf16 rounding.
  * A NaN code is not an error: it propagates into the outputs of the rows that
- * read it.  Errors as attn_fwd, with ATTN_ERR_UNSUPPORTED for d != 128.
+ * read it.  Descales live in device memory and are not read by the host: each
+ * must be finite, and q_descale * k_descale >= 0 for every head.  A zero
+ * descale stands for an all-zero head (zero scores: uniform attention over the
+ * visible keys; zero values from v) and is computed exactly; a head whose
+ * q_descale * k_descale is negative or not finite gets NaN in its O and LSE
+ * rows instead of a silently wrong result.  Errors as attn_fwd, with
+ * ATTN_ERR_UNSUPPORTED for d != 128.
  */
 int attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
                  const float* k_descale, const float* v_descale, void* o, float* lse,
                  int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* stream);
 
 /* Static description of a return code; for ATTN_ERR_HIP, the HIP error text
- * of the last failure on the calling thread.  Never NULL. */
+ * of the last failure on the calling thread.  Never NULL.  ([EVOL] §7,
+ * pitfall 1: a request the fast path cannot serve must surface as an error the
+ * caller can read, not turn silently into a slow fallback; every entry point
+ * therefore returns a code, and this call names it.) */
 const char* attn_strerror(int code);
 
 /* ATTN_OK when device `device` exists and is a gfx950 part this library was

@@ -155,8 +155,7 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
         _check_bf16("out", out, (B, Hq, N, d))
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
+    _check_f32("lse", lse, (B, Hq, N))
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if window is None:
         rc = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
@@ -184,14 +183,17 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     for name, t, shp in (("q", q, (B, Hq, N, d)), ("k", k, (B, Hkv, N, d)), ("v", v, (B, Hkv, N, d)),
                          ("o", o, (B, Hq, N, d)), ("do", do, (B, Hq, N, d))):
         _check_bf16(name, t, shp)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, Hq, N]")
+    _check_f32("lse", lse, (B, Hq, N))
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_bf16("dq", dq, (B, Hq, N, d))
+    _check_bf16("dk", dk, (B, Hkv, N, d))
+    _check_bf16("dv", dv, (B, Hkv, N, d))
     need = bwd_workspace_bytes(B, Hq, Hkv, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ws_bytes = workspace.numel() * workspace.element_size()
     if window is None:
@@ -211,6 +213,13 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 def _check_f32(name: str, t: torch.Tensor, shape) -> None:
     if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape {tuple(shape)}")
+
+
+def _check_workspace(t: torch.Tensor) -> None:
+    """A caller-supplied workspace must be device memory in one piece (its size
+    is checked by the library against what the call needs)."""
+    if not torch.is_tensor(t) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA tensor")
 
 
 def bwd_preprocess(o: torch.Tensor, do: torch.Tensor, delta: Optional[torch.Tensor] = None,
@@ -323,6 +332,7 @@ def fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool =
     need = decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace)
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
     rc = lib().attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk,
                                d, int(bool(causal)), -1 if window is None else int(window), tau,
@@ -410,9 +420,13 @@ def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_bf16("dq", dq, (Hq, T, d))
+    _check_bf16("dk", dk, (Hkv, T, d))
+    _check_bf16("dv", dv, (Hkv, T, d))
     if workspace is None:
         workspace = torch.empty(max(bwd_varlen_workspace_bytes(Hq, T, d), 16), dtype=torch.uint8,
                                 device=q.device)
+    _check_workspace(workspace)
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
     rc = lib().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
                                _ptr(dk), _ptr(dv), _ptr(cu), _ptr(workspace),
@@ -443,6 +457,9 @@ def bwd_grads_varlen(q, k, v, do, lse, delta, cu_seqlens, max_seqlen: Optional[i
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_bf16("dq", dq, (Hq, T, d))
+    _check_bf16("dk", dk, (Hkv, T, d))
+    _check_bf16("dv", dv, (Hkv, T, d))
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
     rc = lib().attn_bwd_grads_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(delta),
                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu), B, T, max_seqlen, Hq,

@@ -20,9 +20,6 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
-# stand-alone HBM read-rate probe (context for memory-bound rooflines)
-PROBE_SRC = "hbm_read_probe.hip"
-PROBE_PATH = os.path.join(PKG_DIR, "hbm_read_probe")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fwd_fp8.hip"]
 HEADERS = ["attn_device.h", "attn_launch.h", "attn_layout.h"]
@@ -71,12 +68,6 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking libattn.so failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
-    cmd = [hipcc(), *DEVICE, *COMMON, os.path.join(CSRC, PROBE_SRC), "-o", PROBE_PATH]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"compiling {PROBE_SRC} failed:\n{r.stdout}\n{r.stderr}")
     return LIB_PATH
 
 

@@ -3,10 +3,11 @@
 // Method (page "从“算力黑洞”到“效率革命”：大模型Attention的演进之路", §4, and page
 // "6.1 … 長上下文擴展技術：FlashAttention、RoPE 與稀疏注意力", §2.2): Q, K and V
 // are cut into blocks along the sequence; a block of query rows is held on
-// chip while K/V tiles stream past it, and for each tile the four steps
-// "score -> update the row max -> accumulate the exp-sum -> accumulate the
-// weighted V" run without the N x N scores ever leaving the chip.  Only O and
-// the per-row log-sum-exp are written.
+// chip while K/V tiles stream past it.  Each tile's scores are formed, the
+// row maxima raised where the tile holds larger scores, the exponential sums
+// carried forward under the new maxima, and the tile's values added with
+// their weights -- all on chip, so the N x N scores never reach device memory.
+// Only O and the per-row log-sum-exp are written.
 //
 // gfx950 mapping
 //   * one workgroup = NW waves x 32 query rows of one (batch, head); each wave

@@ -109,8 +109,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
   const uint8_t* Qp = Q + (size_t)bh * N * kF8D;
   const uint8_t* Kp = K + kv_row0 * kF8D;
   const uint8_t* Vp = V + kv_row0 * kF8D;
-  // scores in log2 units: tau * log2(e) * q_descale * k_descale
-  const float scale_log2 = tau_log2e * q_descale[bh] * k_descale[b * Hkv + hk];
+  // scores in log2 units: tau * log2(e) * q_descale * k_descale.  The running
+  // maximum is taken over the unscaled scores and multiplied afterwards, which
+  // needs a positive factor.  A zero descale stands for an all-zero head: every
+  // score is 0 and the attention is uniform over the visible keys; the smallest
+  // normal factor gives exactly that to within 2^-100 of a score (|raw score| <
+  // 448^2 * 128 < 2^25) and keeps masked keys at -inf (a zero factor would turn
+  // them into NaN).  A negative product or a non-finite factor has no
+  // meaningful maximum here: the head's O and LSE become NaN.
+  const float qk = q_descale[bh] * k_descale[b * Hkv + hk];
+  float scale_log2 = tau_log2e * qk;
+  if (qk == 0.f) scale_log2 = __FLT_MIN__;
+  else if (!(qk > 0.f) || !(scale_log2 < INFINITY)) scale_log2 = __builtin_nanf("");
   const float vds = v_descale[b * Hkv + hk];
 
   const int q0 = qb * kF8BR;

@@ -16,7 +16,7 @@ import torch
 
 from oracle import (attention_backward, attention_forward, attention_probs,
                     backward_dq_rows, bf_backward, bf_forward, default_scale,
-                    forward_rows)
+                    forward_rows, probs_rows)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -307,6 +307,28 @@ def test_row_samplers_match_full():
             assert torch.allclose(lrow, lse[0, h, rows], atol=1e-14)
             assert torch.allclose(backward_dq_rows(q, k, v, do, causal, None, 0, h, rows),
                                   dq[0, h, rows], atol=1e-14)
+
+
+@pytest.mark.parametrize("nq", [10, 4], ids=["square", "decode"])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_probability_rows_match_bruteforce(causal, nq):
+    """P itself, pinned to the scalar brute force: with V the identity (d = N_k)
+    the brute force's output row i is sum_j P_ij e_j, i.e. row i of P.  Covers
+    grouped heads (4 query heads on 2 K/V heads) and, with N_q = 4 < N_k = 10,
+    queries at the last positions (decode alignment).  Both the full matrix
+    (``attention_probs``) and selected rows (``probs_rows``) are checked."""
+    Hq, Hkv, Nk = 4, 2, 10
+    q, k = rnd(61, 1, Hq, nq, Nk), rnd(62, 1, Hkv, Nk, Nk)
+    eye = torch.eye(Nk, dtype=torch.float64).expand(1, Hkv, Nk, Nk).contiguous()
+    bo, _ = bf_forward(q, k, eye, causal, 0.37)
+    bp = torch.tensor(bo, dtype=torch.float64)
+    assert torch.allclose(attention_probs(q, k, causal, 0.37), bp, atol=1e-13)
+    for h in range(Hq):
+        rows = [nq - 1, 0, nq // 2]
+        assert torch.allclose(probs_rows(q, k, causal, 0.37, 0, h, rows), bp[0, h, rows], atol=1e-13)
+    if causal and nq < Nk:
+        # the first decode query sits at position Nk - nq: it sees keys 0 .. Nk - nq only
+        assert bool((bp[0, :, 0, Nk - nq + 1:] == 0).all()) and bool((bp[0, :, 0, :Nk - nq + 1] > 0).all())
 
 
 def test_row_blocking_does_not_change_results():

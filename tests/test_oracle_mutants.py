@@ -46,6 +46,20 @@ MUTANTS = {
         "ob, lb = attention_forward(q[None, :, s0:s1], k[None, :, :s1], v[None, :, :s1],"),
     "varlen_skips_first_sequence": ("for s0, s1 in zip(cu, cu[1:]):", "for s0, s1 in zip(cu[1:], cu[2:]):"),
     "varlen_dk_dv_swapped": ("g[0][0], g[1][0], g[2][0]", "g[0][0], g[2][0], g[1][0]"),
+    "probs_rows_top_left_alignment": (
+        "p, _ = _row_probs(to_f64(q[b, h])[rows_t], to_f64(k[b, g]), rows_t + (k.shape[2] - q.shape[2]),",
+        "p, _ = _row_probs(to_f64(q[b, h])[rows_t], to_f64(k[b, g]), rows_t,"),
+    "probs_rows_modulo_heads": (
+        "    g = h // (Hq // Hkv)\n    d = q.shape[-1]\n    tau = default_scale(d) if scale is None else float(scale)\n"
+        "    rows_t = torch.as_tensor(list(rows), dtype=torch.int64)\n    p, _ = _row_probs(",
+        "    g = h % Hkv\n    d = q.shape[-1]\n    tau = default_scale(d) if scale is None else float(scale)\n"
+        "    rows_t = torch.as_tensor(list(rows), dtype=torch.int64)\n    p, _ = _row_probs("),
+    "attention_probs_top_left_alignment": (
+        "rows = torch.arange(N, dtype=torch.int64) + (k.shape[2] - N)               # positions",
+        "rows = torch.arange(N, dtype=torch.int64)"),
+    "attention_probs_drops_scale": (
+        "out[b, h], _ = _row_probs(q[b, h], k[b, h // G], rows, causal, tau, window)",
+        "out[b, h], _ = _row_probs(q[b, h], k[b, h // G], rows, causal, 1.0, window)"),
 }
 
 
@@ -109,6 +123,20 @@ def pins_pass(mod) -> bool:
             for x, y in zip(g, bg):
                 if not torch.allclose(x, torch.tensor(y, dtype=torch.float64)[0], atol=1e-10):
                     return False
+        # rows of P (attention_probs, probs_rows) against the brute force with V = I
+        Nk = 10
+        for nq in (10, 4):
+            pq, pk = rnd(61, 1, 4, nq, Nk), rnd(62, 1, 2, Nk, Nk)
+            eye = torch.eye(Nk, dtype=torch.float64).expand(1, 2, Nk, Nk).contiguous()
+            for causal in (True, False):
+                bp = torch.tensor(bf_forward(pq, pk, eye, causal, 0.37)[0], dtype=torch.float64)
+                if not torch.allclose(mod.attention_probs(pq, pk, causal, 0.37), bp, atol=1e-13):
+                    return False
+                for h in range(4):
+                    rows = [nq - 1, 0, nq // 2]
+                    if not torch.allclose(mod.probs_rows(pq, pk, causal, 0.37, 0, h, rows),
+                                          bp[0, h, rows], atol=1e-13):
+                        return False
     except Exception:
         return False
     return True
