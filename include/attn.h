@@ -68,6 +68,8 @@ extern "C" {
 #define ATTN_ERR_SCALE       5  /* scale not finite or not > 0                      */
 #define ATTN_ERR_HIP         6  /* a HIP runtime call or kernel launch failed; the
                                    message is available from attn_strerror(6)       */
+#define ATTN_ERR_SCRATCH     7  /* attn_fwd_decode_static: the problem's partials
+                                   exceed ATTN_DECODE_STATIC_SCRATCH_BYTES         */
 
 /*
  * Forward pass ([EVOL] §4, [LONGCTX] §2.2).
@@ -194,6 +196,31 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
                     int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window,
                     float scale, int num_splits, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/*
+ * attn_fwd_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It computes exactly what attn_fwd_decode computes (same
+ * kernels, same chunking for the same num_splits, bitwise the same outputs),
+ * taking the per-chunk partials from a static buffer that the library holds in
+ * device memory for the life of the process: ATTN_DECODE_STATIC_SCRATCH_BYTES
+ * per GPU, reserved on every GPU the library runs on.  The call allocates
+ * nothing and frees nothing.
+ *   - Problems whose partials (attn_fwd_decode_workspace_bytes for the same
+ *     arguments) exceed that size return ATTN_ERR_SCRATCH before any device
+ *     work.
+ *   - Every call on one GPU uses that GPU's one buffer: calls that can overlap
+ *     on one GPU (different streams, or different host threads without an
+ *     ordering between them) race on it and give undefined results; order them
+ *     on one stream or with events.  Calls on different GPUs do not interact.
+ *   - The buffer needs no initialisation: each call writes every partial it
+ *     reads, so the previous call's contents never leak into a result.
+ * Arguments, layouts and the other errors are those of attn_fwd_decode.
+ */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int window,
+                           float scale, int num_splits, void* stream);
 
 /*
  * Packed variable-length batches (page "从“算力黑洞”到“效率革命”：大模型Attention的

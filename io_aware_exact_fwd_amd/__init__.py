@@ -21,7 +21,7 @@ import torch  # loads the HIP runtime that libattn.so then binds to
 
 __all__ = [
     "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads", "fwd_decode",
-    "decode_workspace_bytes", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
+    "decode_workspace_bytes", "fwd_decode_static", "DECODE_STATIC_SCRATCH_BYTES", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
     "bwd_grads_varlen", "fwd_fp8", "attention", "attention_varlen",
     "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
@@ -33,9 +33,11 @@ EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_prepro
             "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window",
             "attn_fwd_decode", "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
             "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes", "attn_bwd_grads_varlen",
-            "attn_fwd_fp8")
+            "attn_fwd_fp8", "attn_fwd_decode_static")
 
 ATTN_OK = 0
+# bytes of the static decode scratch behind attn_fwd_decode_static (include/attn.h)
+DECODE_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class AttnError(RuntimeError):
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_grads_window.restype = i
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
     L.attn_fwd_decode.restype = i
+    L.attn_fwd_decode_static.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    L.attn_fwd_decode_static.restype = i
     L.attn_fwd_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_fwd_decode_workspace_bytes.restype = sz
     L.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
@@ -342,6 +346,37 @@ def fwd_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool =
         raise AttnError(rc, "attn_fwd_decode")
     return out, lse
 
+
+
+def fwd_decode_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                      scale: Optional[float] = None, window: Optional[int] = None,
+                      num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fwd_decode without a workspace (attn_fwd_decode_static): the per-chunk
+    partials live in the library's static per-GPU scratch, so with ``out`` and
+    ``lse`` given nothing is allocated.  Calls that may overlap on one GPU race
+    on that scratch (see include/attn.h)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _check_bf16("q", q, (B, Hq, Nq, d))
+    _check_bf16("k", k, (B, Hkv, Nk, d))
+    _check_bf16("v", v, (B, Hkv, Nk, d))
+    out = torch.empty_like(q) if out is None else out
+    _check_bf16("out", out, (B, Hq, Nq, d))
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    _check_f32("lse", lse, (B, Hq, Nq))
+    tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = lib().attn_fwd_decode_static(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv,
+                                      Nq, Nk, d, int(bool(causal)),
+                                      -1 if window is None else int(window), tau, int(num_splits),
+                                      _stream(stream))
+    if rc != ATTN_OK:
+        raise AttnError(rc, "attn_fwd_decode_static")
+    return out, lse
 
 
 # ---------------------------------------------------------------------------

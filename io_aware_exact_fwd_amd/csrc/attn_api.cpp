@@ -269,6 +269,33 @@ ATTN_EXPORT int attn_fwd_decode(const void* q, const void* k, const void* v, voi
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd_decode launch");
 }
 
+ATTN_EXPORT int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o,
+                                       float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                       int causal, int window, float scale, int num_splits,
+                                       void* stream) {
+  static_assert(attn::kDecodeStaticScratchBytes == ATTN_DECODE_STATIC_SCRATCH_BYTES,
+                "header and library agree on the static scratch size");
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+  int rc = check_decode(B, Hq, Hkv, Nq, Nk, d);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
+  int chunk = 0;
+  const int splits = attn::decode_splits(B, Hq, Hkv, Nq, Nk, num_splits, &chunk);
+  if (attn::decode_workspace_bytes(B, Hq, Nq, d, splits) > attn::kDecodeStaticScratchBytes)
+    return ATTN_ERR_SCRATCH;
+  if ((rc = check_scale(scale))) return rc;
+  if ((rc = current_device_check())) return rc;
+  float* scratch = nullptr;
+  hipError_t e = attn::decode_static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "attn_fwd_decode_static scratch lookup");
+  attn::DecodeArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal != 0, scale,
+                     window < 0 ? -1 : window, splits, chunk, scratch};
+  e = attn::launch_decode(a, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_fwd_decode_static launch");
+}
+
 // Shapes of a packed variable-length call: B sequences, `total` packed rows per
 // head, none longer than max_seqlen.  total == 0 is an empty batch.
 static int check_varlen(int B, int total, int max_seqlen, int Hq, int Hkv, int d) {
@@ -377,6 +404,9 @@ ATTN_EXPORT const char* attn_strerror(int code) {
     case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_HIP: return g_hip_msg;
+    case ATTN_ERR_SCRATCH:
+      return "the problem needs more than ATTN_DECODE_STATIC_SCRATCH_BYTES (32 MiB) of decode "
+             "partials: call attn_fwd_decode with a workspace, or ask for fewer splits";
     default: return "unknown attn error code";
   }
 }

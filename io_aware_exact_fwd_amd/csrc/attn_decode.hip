@@ -35,7 +35,18 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+#include <mutex>
+
 namespace attn {
+
+// The per-chunk partials of attn_fwd_decode_static, for callers that cannot
+// allocate: a fixed array in device memory that the library holds for the
+// life of the process, one copy per GPU (each GPU's copy has its own address,
+// looked up once per device by decode_static_scratch below).  Host code never
+// passes this name to a kernel -- on the host it is only a stand-in for the
+// symbol -- but the device address that lookup returns.
+static __device__ __align__(256) float scratch[kDecodeStaticScratchBytes / sizeof(float)];
+
 namespace {
 
 constexpr int kDecNW = 4;            // waves per workgroup, 32 keys of each tile each
@@ -332,6 +343,31 @@ int decode_splits(int B, int Hq, int Hkv, int Nq, int Nk, int requested, int* ch
   s = (n_tiles + tiles_per - 1) / tiles_per;        // no empty chunk
   *chunk = tiles_per * kDecBC;
   return s;
+}
+
+hipError_t decode_static_scratch(float** out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<float*> addr[kMaxDev];
+  static std::mutex lookup;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  float* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> g(lookup);
+    p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      void* a = nullptr;
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));   // with this device current
+      if (e != hipSuccess) return e;
+      if (!a) return hipErrorInvalidSymbol;
+      p = (float*)a;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

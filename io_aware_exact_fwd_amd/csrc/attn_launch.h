@@ -122,6 +122,12 @@ inline size_t decode_workspace_bytes(int B, int Hq, int Nq, int d, int n_splits)
   return (size_t)n_splits * B * Hq * Nq * (d + 1) * sizeof(float);
 }
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Bytes of the library's static decode scratch (one copy per GPU).
+constexpr size_t kDecodeStaticScratchBytes = size_t{32} << 20;
+// Device address of the current GPU's static decode scratch, looked up on the
+// first call on each device and cached.  The scratch needs no clearing: every
+// decode launch writes each partial it later reads.
+hipError_t decode_static_scratch(float** out);
 // The backward's stages.  Each reads the BwdArgs fields it needs (delta must
 // be set for all of them).  launch_bwd_grads runs dK/dV and dQ in one launch;
 // launch_bwd is launch_bwd_pre followed by launch_bwd_grads.

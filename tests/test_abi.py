@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
                                            "attn_fwd_decode",
                                            "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
                                            "attn_bwd_varlen", "attn_bwd_grads_varlen", "attn_fwd_fp8",
-                                           "attn_bwd_varlen_workspace_bytes"])
+                                           "attn_bwd_varlen_workspace_bytes",
+                                           "attn_fwd_decode_static"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -136,7 +137,7 @@ def test_stage_argument_errors(L):
 
 
 def test_strerror(L):
-    for code in range(0, 7):
+    for code in range(0, 8):
         s = L.attn_strerror(code)
         assert s and len(s) > 1
     assert b"unknown" in L.attn_strerror(99)
@@ -196,6 +197,25 @@ def test_decode_validation_and_workspace(L):
     assert L.attn_fwd_decode(*args, 1, 4, 4, 1, 64, 64, 1, -1, -1.0, 0, A, 1 << 20, None) == 5
     assert L.attn_fwd_decode(A, A, MIS, A, A, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, A, 1 << 20, None) == 3
 
+
+
+def test_decode_static_validation(L):
+    """The decode call without a workspace: the same argument checks as
+    attn_fwd_decode, and a problem whose partials exceed the static scratch is
+    refused (ATTN_ERR_SCRATCH) before any device work."""
+    f = L.attn_fwd_decode_static
+    ws = L.attn_fwd_decode_workspace_bytes
+    #        q  k  v  o  lse B   Hq  Hkv Nq  Nk    d    causal win scale splits
+    assert f(A, A, A, A, None, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, None) == 1
+    assert f(A, A, A, A, A, 1, 4, 4, 5, 4, 64, 1, -1, 0.1, 0, None) == 2           # Nq > Nk
+    assert f(A, A, A, A, A, 1, 4, 3, 1, 64, 64, 1, -1, 0.1, 0, None) == 2          # Hq % Hkv
+    assert f(A, A, A, A, A, 1, 4, 4, 1, 64, 96, 1, -1, 0.1, 0, None) == 3          # d
+    assert f(A, A, MIS, A, A, 1, 4, 4, 1, 64, 64, 1, -1, 0.1, 0, None) == 3        # alignment
+    assert f(A, A, A, A, A, 1, 4, 4, 1, 64, 64, 1, -1, -1.0, 0, None) == 5         # scale
+    big = (64, 64, 64, 16, 4096, 128)
+    assert ws(*big, 32) > 32 << 20
+    assert f(A, A, A, A, A, *big, 1, -1, 0.1, 32, None) == 7                       # scratch too small
+    assert b"static" in L.attn_strerror(7) or b"STATIC" in L.attn_strerror(7)
 
 
 def test_varlen_validation_and_workspace(L):
