@@ -44,16 +44,17 @@ PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS
 
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "io_aware_exact_fwd_amd", "csrc")
-# source files each kernel is compiled from (their hash decides whether recorded
-# counters still describe the kernel)
+# source files each kernel is compiled and launched from (their hash decides
+# whether recorded counters still describe the kernel)
+_SHARED = ("attn_device.h", "attn_layout.h", "attn_launch.h")
 KERNEL_SOURCES = {
-    "attn_fwd_kernel": ("attn_device.h", "attn_layout.h", "attn_fwd.hip"),
-    "bwd_pre_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
-    "bwd_dkdv_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
-    "bwd_dq_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
-    "bwd_grads_kernel": ("attn_device.h", "attn_layout.h", "attn_bwd.hip"),
-    "attn_decode_split_kernel": ("attn_device.h", "attn_layout.h", "attn_decode.hip"),
-    "attn_fwd_fp8_kernel": ("attn_device.h", "attn_layout.h", "attn_fwd_fp8.hip"),
+    "attn_fwd_kernel": _SHARED + ("attn_fwd.hip",),
+    "bwd_pre_kernel": _SHARED + ("attn_bwd.hip",),
+    "bwd_dkdv_kernel": _SHARED + ("attn_bwd.hip",),
+    "bwd_dq_kernel": _SHARED + ("attn_bwd.hip",),
+    "bwd_grads_kernel": _SHARED + ("attn_bwd.hip",),
+    "attn_decode_split_kernel": _SHARED + ("attn_decode.hip",),
+    "attn_fwd_fp8_kernel": _SHARED + ("attn_fwd_fp8.hip",),
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 

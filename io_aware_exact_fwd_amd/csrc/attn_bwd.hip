@@ -100,17 +100,29 @@ __device__ __forceinline__ void dkdv_block(
   // heaviest key blocks (the first ones under the causal mask) first; when
   // B*Hkv is a multiple of 8 all key blocks of one K/V head share an XCD, so
   // the Q/dO tiles they all read stay in that XCD's L2
-  int bhk, kb;
-  if (xcd_remap) {
-    const int hx = BHkv >> 3;
-    const int i = w >> 3;
-    bhk = (w & 7) * hx + (i % hx);
-    kb = i / hx;
+  int b, hk, kb;
+  if (pk.cu && BHkv / Hkv <= kMaxPackedSeqs) {
+    // packed: real key blocks only, heaviest (most query tiles after them) first
+    PackedUnits pu;
+    pu.init(pk, BHkv / Hkv, Nmax, C::kBKV);
+    int level;
+    if (!pu.unit(w, Hkv, b, hk, level)) return;
+    const int len = seq_span(pk, Nmax, b).len;
+    kb = (len + C::kBKV - 1) / C::kBKV - 1 - level;
   } else {
-    bhk = w % BHkv;
-    kb = w / BHkv;
+    int bhk;
+    if (xcd_remap) {
+      const int hx = BHkv >> 3;
+      const int i = w >> 3;
+      bhk = (w & 7) * hx + (i % hx);
+      kb = i / hx;
+    } else {
+      bhk = w % BHkv;
+      kb = w / BHkv;
+    }
+    b = bhk / Hkv;
+    hk = bhk - b * Hkv;
   }
-  const int b = bhk / Hkv, hk = bhk - b * Hkv;
   const SeqSpan sp = seq_span(pk, Nmax, b);
   const int N = sp.len;                  // rows of this sequence
   const int k0 = kb * C::kBKV;
@@ -353,18 +365,28 @@ __device__ __forceinline__ void dq_block(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
 
-  int bh, qrank;
-  if (xcd_remap) {
-    const int hx = BH >> 3;
-    const int i = w >> 3;
-    bh = (w & 7) * hx + (i % hx);
-    qrank = i / hx;
+  int b, h, qb;
+  if (pk.cu && BH / Hq <= kMaxPackedSeqs) {
+    // packed: real query blocks only, heaviest (most key tiles) first
+    PackedUnits pu;
+    pu.init(pk, BH / Hq, Nmax, C::kBQ);
+    if (!pu.unit(w, Hq, b, h, qb)) return;
   } else {
-    bh = w % BH;
-    qrank = w / BH;
+    int bh, qrank;
+    if (xcd_remap) {
+      const int hx = BH >> 3;
+      const int i = w >> 3;
+      bh = (w & 7) * hx + (i % hx);
+      qrank = i / hx;
+    } else {
+      bh = w % BH;
+      qrank = w / BH;
+    }
+    qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
+    b = bh / Hq;
+    h = bh - b * Hq;
   }
-  const int qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
-  const int b = bh / Hq, h = bh - b * Hq, hk = h / G;
+  const int hk = h / G;
   const SeqSpan sp = seq_span(pk, Nmax, b);
   const int N = sp.len;                  // rows of this sequence
   const int q0 = qb * C::kBQ;
@@ -500,7 +522,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 }
 
 // dK/dV and dQ in one launch: workgroups [0, n_dkdv) are dK/dV blocks and the
-// rest dQ blocks.  The two halves are independent (both read only the inputs,
+// rest dQ blocks (a packed batch of up to kMaxPackedSeqs sequences: its real
+// dK/dV units, then its real dQ units, then empty workgroups).  The two halves are independent (both read only the inputs,
 // LSE and D), so dQ blocks fill the CUs that dK/dV blocks release instead of
 // waiting for the whole dK/dV grid to drain.  Both halves use 8 waves.
 template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL>
@@ -514,12 +537,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   static_assert(2 * NWK == NW, "both halves run the same number of waves");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int w = blockIdx.x;
-  if (w < n_dkdv)
+  int split = n_dkdv;
+  if (pk.cu && BHkv / Hkv <= kMaxPackedSeqs) {
+    // packed: the real dK/dV units come first, then the real dQ units; the
+    // rest of the grid (sized for the longest sequence) is empty
+    PackedUnits pu;
+    pu.init(pk, BHkv / Hkv, N, DkdvCfg<D, NWK>::kBKV);
+    split = (int)pu.at_or_above(0, Hkv);
+  }
+  if (w < split)
     dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
                                       scale_log2, xcd_kv, window, pk, w, smem);
   else
     dq_block<D, BC, NW, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
-                                       scale_log2, xcd_q, window, pk, w - n_dkdv, smem);
+                                       scale_log2, xcd_q, window, pk, w - split, smem);
 }
 
 // Dynamic LDS beyond 64 KB, allowed once per kernel instance and device.
@@ -552,8 +583,9 @@ struct LaunchDkdv {
     if (attr != hipSuccess) return attr;
     const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
     const int BHkv = a.B * a.Hkv;
-    const long long grid = (long long)BHkv * n_kb;
+    const long long grid = packed_grid(a.pack, a.B, a.Hkv, CK::kBKV, (long long)BHkv * n_kb);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), CK::kLdsBytes, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv,
@@ -573,8 +605,9 @@ struct LaunchDq {
     if (attr != hipSuccess) return attr;
     const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
     const int BH = a.B * a.Hq;
-    const long long grid = (long long)BH * n_qb;
+    const long long grid = packed_grid(a.pack, a.B, a.Hq, CQ::kBQ, (long long)BH * n_qb);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CQ::kThreads), CQ::kLdsBytes, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.N, BH, a.Hq,
@@ -599,8 +632,10 @@ struct LaunchGrads {
     const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
     const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
     const long long n_dkdv = (long long)BHkv * n_kb;
-    const long long grid = n_dkdv + (long long)BH * n_qb;
+    const long long grid = packed_grid(a.pack, a.B, a.Hkv, CK::kBKV, n_dkdv) +
+                           packed_grid(a.pack, a.B, a.Hq, CQ::kBQ, (long long)BH * n_qb);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CK::kThreads), lds, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,

@@ -107,6 +107,115 @@ __device__ __forceinline__ size_t head_stride(const Packing& p, int N) {
   return p.cu ? (size_t)p.T : (size_t)N;
 }
 
+// ---------------------------------------------------------------------------
+// Work units of a packed batch, heaviest first.
+//
+// A grid sized for B sequences of the longest length holds many workgroups
+// whose block lies past the end of a shorter sequence.  Instead of mapping
+// the workgroup index to (sequence, head, block) arithmetically and returning
+// from those, a packed launch enumerates only the real units: sequence b owns
+// n_b = ceil(len_b / BS) blocks of BS rows, and block k of it gets a level L
+// (0 <= L < n_b) that grows with its cost (the caller picks L = k or
+// L = n_b - 1 - k).  Units are ordered by level, highest first, then by
+// sequence, then by head (Hn per sequence); with
+//     C(L) = Hn * sum_b max(0, n_b - L)
+// units at levels >= L, unit w sits at the largest level L with C(L) > w, and
+// its rank among that level's units is w - C(L+1).  Every workgroup index past
+// C(0) is empty and comes after all real ones.  Each wave evaluates this
+// itself, with the block counts of up to kMaxPackedSeqs sequences held in its
+// lanes (b = lane + 64 j); the lengths are clamped exactly as seq_span does.
+// ---------------------------------------------------------------------------
+static_assert(kMaxPackedSeqs % 64 == 0, "whole waves of sequences");
+
+// Sum / max of v over the 64 lanes of a wave (every lane active), returned in
+// a scalar register: four DPP steps give every lane its 16-lane row's result
+// (swap neighbours, swap pairs, mirror each half row, mirror the row), and the
+// four rows are combined through readlane.
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true);    // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true);    // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true);   // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true);   // row_mirror
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, true));
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+struct PackedUnits {
+  int n[kMaxPackedSeqs / 64];   // blocks of sequence lane + 64 j (0 past B)
+  int nmax;                     // most blocks of any sequence (wave-uniform)
+
+  // All boundary loads are issued before any is used (indices past B are
+  // clamped to B, a valid entry, and their counts zeroed), so the table costs
+  // one memory round trip.
+  __device__ __forceinline__ void init(const Packing& p, int B, int Nmax, int BS) {
+    const int lane = threadIdx.x & 63;
+    int lo[kMaxPackedSeqs / 64], hi[kMaxPackedSeqs / 64];
+#pragma unroll
+    for (int j = 0; j < kMaxPackedSeqs / 64; ++j) {
+      const int b = min(lane + 64 * j, B);
+      lo[j] = p.cu[b];
+      hi[j] = p.cu[min(b + 1, B)];
+    }
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPackedSeqs / 64; ++j) {
+      const int c0 = min(max(lo[j], 0), p.T);
+      const int c1 = min(max(hi[j], c0), p.T);
+      const int len = min(c1 - c0, Nmax);
+      n[j] = lane + 64 * j < B ? (len + BS - 1) / BS : 0;
+      m = max(m, n[j]);
+    }
+    nmax = wave_max_i32(m);
+  }
+  // units at levels >= L (wave-uniform)
+  __device__ __forceinline__ long long at_or_above(int L, int Hn) const {
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxPackedSeqs / 64; ++j) s += max(0, n[j] - L);
+    return (long long)wave_sum_i32(s) * Hn;
+  }
+  // Unit w: false when w is past the last unit; else its sequence, head and level.
+  __device__ __forceinline__ bool unit(long long w, int Hn, int& b, int& h, int& level) const {
+    if (w >= at_or_above(0, Hn)) return false;
+    int lo = 0, hi = nmax - 1;   // at_or_above(lo) > w throughout
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (at_or_above(mid, Hn) > w) lo = mid;
+      else hi = mid - 1;
+    }
+    const long long r = w - at_or_above(lo + 1, Hn);
+    const int rank = (int)(r / Hn);
+    h = (int)(r - (long long)rank * Hn);
+    level = lo;
+    // the rank-th sequence (in index order) with more than lo blocks
+    int seen = 0;
+    b = -1;
+#pragma unroll
+    for (int j = 0; j < kMaxPackedSeqs / 64; ++j) {
+      const unsigned long long m = __ballot(n[j] > lo);
+      const int c = __popcll(m);
+      if (b < 0 && rank < seen + c) {
+        unsigned long long mm = m;
+        for (int t = seen; t < rank; ++t) mm &= mm - 1;   // drop the lower set bits
+        b = 64 * j + __builtin_ctzll(mm);
+      }
+      seen += c;
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    h = __builtin_amdgcn_readfirstlane(h);
+    level = __builtin_amdgcn_readfirstlane(level);
+    return true;
+  }
+};
+
 // Instruction classes for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;

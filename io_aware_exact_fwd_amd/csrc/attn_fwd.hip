@@ -83,20 +83,28 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   const int hi = lane >> 5;
 
   // ---- workgroup -> (batch*head, query block) ----
-  int bh, qrank;
+  int b, h, qb;
   const int w = blockIdx.x;
-  if (xcd_remap) {
-    const int hx = BH >> 3;
-    const int i = w >> 3;
-    bh = (w & 7) * hx + (i % hx);
-    qrank = i / hx;
+  if (pk.cu && BH / Hq <= kMaxPackedSeqs) {
+    // packed: real blocks only, heaviest (most key tiles) first
+    PackedUnits pu;
+    pu.init(pk, BH / Hq, Nmax, C::kBR);
+    if (!pu.unit(w, Hq, b, h, qb)) return;
   } else {
-    bh = w % BH;
-    qrank = w / BH;
+    int bh, qrank;
+    if (xcd_remap) {
+      const int hx = BH >> 3;
+      const int i = w >> 3;
+      bh = (w & 7) * hx + (i % hx);
+      qrank = i / hx;
+    } else {
+      bh = w % BH;
+      qrank = w / BH;
+    }
+    qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
+    b = bh / Hq;
+    h = bh - b * Hq;
   }
-  const int qb = CAUSAL ? (n_qb - 1 - qrank) : qrank;
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
   const int hk = h / G;
   // this pair's sequence: N rows of queries and keys (packed: its own length)
   const SeqSpan sp = seq_span(pk, Nmax, b);
@@ -280,8 +288,9 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   using C = FwdCfg<D, BC, NW>;
   const int n_qb = (a.N + C::kBR - 1) / C::kBR;
   const int BH = a.B * a.Hq;
-  const long long grid = (long long)BH * n_qb;
+  const long long grid = packed_grid(a.pack, a.B, a.Hq, C::kBR, (long long)BH * n_qb);
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (grid == 0) return hipSuccess;
   auto kern = attn_fwd_kernel<D, BC, NW, WPE, CAUSAL, LOCAL, LAG>;
   // more than 64 KB of dynamic LDS has to be allowed per kernel instance and device
   static std::atomic<uint64_t> lds_set{0};

@@ -40,6 +40,23 @@ inline hipError_t allow_lds_on_device(const void* kern, int bytes, std::atomic<u
 // of 8 each XCD then gets the same heads of every sequence.
 inline int xcd_remap(int units, const Packing& p) { return (units % 8 == 0 && !p.cu) ? 1 : 0; }
 
+// Packed batches of up to this many sequences are launched over their real
+// blocks only (the kernels enumerate them from the boundary table, heaviest
+// first); larger ones take the plain (batch, head, block) grid.
+constexpr int kMaxPackedSeqs = 512;
+
+// Workgroups for `heads` x blocks of BS rows over B sequences: `plain` (every
+// sequence as long as the longest), or for a packed batch of at most
+// kMaxPackedSeqs sequences the smaller bound heads * (ceil(T / BS) + B) on its
+// real blocks (sum over b of ceil(len_b / BS) <= T / BS + B whenever the
+// boundaries rise; rows a malformed table would add past that are not
+// computed, as with any malformed table).
+inline long long packed_grid(const Packing& p, int B, int heads, int BS, long long plain) {
+  if (!p.cu || B > kMaxPackedSeqs) return plain;
+  const long long bound = (long long)heads * (((long long)p.T + BS - 1) / BS + B);
+  return bound < plain ? bound : plain;
+}
+
 struct FwdArgs {
   const void* q;
   const void* k;

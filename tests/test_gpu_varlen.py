@@ -5,8 +5,9 @@ its own attention problem.  Bars as for the fixed-length calls: max |O|
 error <= 1e-2, max |LSE| error <= 1e-3, max |G - G_ref| / max |G_ref| <= 2e-2
 for each gradient.  Cases: empty and one-token sequences, lengths on and off
 tile edges, several tiles per sequence, grouped and multi-query heads,
-d = 64 and 128, windows, and the packed benchmark workload element by
-element.  The packed calls must also be bitwise equal to calling the
+d = 64 and 128, windows, batches of up to 700 sequences on both sides of
+the 512-sequence limit of the per-block launch, and the packed benchmark
+workload element by element.  The packed calls must also be bitwise equal to calling the
 fixed-length entry points on every sequence alone.
 """
 import numpy as np
@@ -20,8 +21,8 @@ from synth_inputs import cu_from_lengths, make_custom_inputs, make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def pack_draw(lengths, Hq, Hkv, d, seed):
-    x = make_custom_inputs(1, Hq, Hkv, sum(lengths), d, seed=seed, with_grad=True)
+def pack_draw(lengths, Hq, Hkv, d, seed, in_scale=1.0):
+    x = make_custom_inputs(1, Hq, Hkv, sum(lengths), d, seed=seed, with_grad=True, in_scale=in_scale)
     x = {n: a[0] for n, a in x.items()}
     x["cu_seqlens"] = cu_from_lengths(lengths)
     return x
@@ -89,6 +90,60 @@ def test_varlen_equals_per_sequence_calls(gpu_lib, causal):
         torch.cuda.synchronize()
         for packed, alone in ((o, so), (lse, sl), (dq, sdq), (dk, sdk), (dv, sdv)):
             assert torch.equal(packed[:, s0:s1], alone[0]), (s0, s1)
+
+
+def _nan_like(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+# (number of sequences, longest, Hq, Hkv, d): batches of at most 512 sequences
+# are launched over their real blocks only (each workgroup finds its sequence,
+# head and block from the table, heaviest first); larger ones over the plain
+# (sequence, head, block) grid.  Outputs start as NaN, so a block that no
+# workgroup computes shows as non-finite rows.  The draws are at half scale:
+# rows of sequences this short average only a few values of V, so |O| comes
+# close to max |V| (about 5 at unit scale), where half a bf16 ulp of the
+# output alone reaches 0.0156; at half scale it stays under the 1e-2 bar.
+MANY = [
+    (40, 1500, 4, 1, 128),     # few long, heterogeneous sequences: heaviest-first order across them
+    (300, 60, 4, 2, 64),       # many short ones, some empty
+    (512, 40, 2, 2, 64),       # the largest batch taken by block
+    (700, 40, 2, 1, 64),       # past it: the plain grid
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("case", MANY, ids=lambda c: "B{}_max{}_Hq{}_Hkv{}_d{}".format(*c))
+def test_varlen_many_sequences(gpu_lib, case, causal):
+    nseq, longest, Hq, Hkv, d = case
+    rng = np.random.default_rng(nseq + longest)
+    lengths = [int(round(np.exp(rng.uniform(0.0, np.log(longest))))) for _ in range(nseq)]
+    for i in range(3, nseq, 11):
+        lengths[i] = 0
+    T = sum(lengths)
+    say(f"varlen many: B={nseq} T={T} longest={max(lengths)} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    x = pack_draw(lengths, Hq, Hkv, d, seed=nseq + 7, in_scale=0.5)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(x["cu_seqlens"]).cuda()
+    o, lse = _nan_like((Hq, T, d), torch.bfloat16), _nan_like((Hq, T), torch.float32)
+    gpu_lib.fwd_varlen(q, k, v, cu, max(lengths), causal=causal, out=o, lse=lse)
+    dq = _nan_like((Hq, T, d), torch.bfloat16)
+    dk, dv = _nan_like((Hkv, T, d), torch.bfloat16), _nan_like((Hkv, T, d), torch.bfloat16)
+    gpu_lib.bwd_varlen(q, k, v, o, lse, do, cu, max(lengths), causal=causal, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    f = {n: to_f64(x[n]) for n in ("q", "k", "v", "do")}
+    cul = x["cu_seqlens"].tolist()
+    ro, rl = varlen_forward(f["q"], f["k"], f["v"], cul, causal)
+    rdq, rdk, rdv = varlen_backward(f["q"], f["k"], f["v"], f["do"], cul, causal)
+    floor = 1e-3 * max(float(t.abs().max()) for t in (rdq, rdk, rdv))
+    errs = {"O": max_abs(dev_f64(o), ro), "LSE": max_abs(dev_f64(lse), rl),
+            "dQ": rel_maxnorm(dev_f64(dq), rdq, floor), "dK": rel_maxnorm(dev_f64(dk), rdk, floor),
+            "dV": rel_maxnorm(dev_f64(dv), rdv, floor)}
+    print(" ".join(f"{kk}={vv:.3g}" for kk, vv in errs.items()))
+    assert errs["O"] <= TOL_O and errs["LSE"] <= TOL_LSE, errs
+    assert max(errs["dQ"], errs["dK"], errs["dV"]) <= TOL_GRAD_REL, errs
 
 
 def test_varlen_device_table_and_stages(gpu_lib):
