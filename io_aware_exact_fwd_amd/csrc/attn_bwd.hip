@@ -523,9 +523,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 
 // dK/dV and dQ in one launch: workgroups [0, n_dkdv) are dK/dV blocks and the
 // rest dQ blocks (a packed batch of up to kMaxPackedSeqs sequences: its real
-// dK/dV units, then its real dQ units, then empty workgroups).  The two halves are independent (both read only the inputs,
-// LSE and D), so dQ blocks fill the CUs that dK/dV blocks release instead of
-// waiting for the whole dK/dV grid to drain.  Both halves use 8 waves.
+// dK/dV units, then its real dQ units, then empty workgroups).  The two
+// halves are independent (both read only the inputs, LSE and D), so dQ blocks
+// fill the CUs that dK/dV blocks release instead of waiting for the whole
+// dK/dV grid to drain.  Both halves use 8 waves.
 template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void bwd_grads_kernel(
