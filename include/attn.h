@@ -236,16 +236,18 @@ int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o,
  *                   cu_seqlens[b] .. cu_seqlens[b+1] - 1 of every head;
  *                   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = total
  *                   (empty sequences allowed)
- *   max_seqlen      the longest sequence (sizes the grid): 1 <= max_seqlen <= total
+ *   max_seqlen      the longest sequence (bounds the grid): 1 <= max_seqlen <= total
  *   window < 0: none; >= 0: as attn_fwd_window, within each sequence
  *   workspace       attn_bwd_varlen: >= attn_bwd_varlen_workspace_bytes(Hq, total, d)
  *                   bytes (fp32 D per packed query row); contents on exit unspecified
  *
- * The boundaries live on the device and are not read by the host.  A table
- * that breaks the rules above (or a sequence longer than max_seqlen) cannot
- * make the kernels access memory outside the [H, total, d] tensors -- every
- * boundary is clamped to [0, total] and every length to max_seqlen -- but the
- * rows it describes wrongly are left unspecified.  total = 0 is an empty batch
+ * The boundaries live on the device and are not read by the host; with up to
+ * 512 sequences each workgroup finds its own (sequence, head, block) among the
+ * table's real blocks, heaviest first.  A table that breaks the rules above
+ * (or a sequence longer than max_seqlen) cannot make the kernels access memory
+ * outside the [H, total, d] tensors -- every boundary is clamped to
+ * [0, total] and every length to max_seqlen -- but the rows it describes
+ * wrongly are left unspecified.  total = 0 is an empty batch
  * and returns ATTN_OK without touching memory.  Other errors as attn_fwd /
  * attn_bwd (ATTN_ERR_SHAPE also for max_seqlen > total, or total * d or
  * Hq * total beyond 2^31 - 1).  Deterministic, like the fixed-length calls.
