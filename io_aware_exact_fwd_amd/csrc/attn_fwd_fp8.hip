@@ -29,6 +29,8 @@
 #include "attn_device.h"
 #include "attn_launch.h"
 
+#include <type_traits>
+
 namespace attn {
 namespace {
 
@@ -162,113 +164,136 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
   issue_tile(0);
   wait_all_memory();
   __syncthreads();
-  for (int j = 0; j < n_tiles; ++j) {
+  // A wave works on tiles [0, n_act): under the causal mask those that start
+  // at or before its last row.  Tiles from n_mask on cross the diagonal or the
+  // ragged end and take the mask.  The unmasked, the masked and the idle tiles
+  // run as three loops -- every wave still issues every tile's loads and meets
+  // every barrier -- so no idle or masked path merges into the accumulators
+  // of the main loop (with such a merge the compiler copies all 64
+  // accumulator registers on every tile).
+  const int n_act = !wave_live ? 0 : (CAUSAL ? min(n_tiles, qw1 / kF8BC + 1) : n_tiles);
+  const int n_mask = CAUSAL ? min(N / kF8BC, (qw0 + 1) / kF8BC) : N / kF8BC;
+  const int n_plain = min(n_act, n_mask);
+  auto tile = [&](int j, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
     const int kstart = j * kF8BC;
-    if (j + 1 < n_tiles) issue_tile(j + 1);
-    if (wave_live && (!CAUSAL || kstart <= qw1)) {
-      const unsigned char* kt = stage(j);
-      const unsigned char* vt = kt + kF8Tile;
+    const unsigned char* kt = stage(j);
+    const unsigned char* vt = kt + kF8Tile;
 
-      // S^T[x] = K_x Q^T: 32 keys x 32 queries, lane holds query column l%32.
-      // Step i is key block i % KB, d half i / KB; the K fragments go through
-      // a ring of kPrefK registers, each read issued kPrefK MFMAs ahead.
-      f32x16 s[KB];
+    // S^T[x] = K_x Q^T: 32 keys x 32 queries, lane holds query column l%32.
+    // Step i is key block i % KB, d half i / KB; the K fragments go through
+    // a ring of kPrefK registers, each read issued kPrefK MFMAs ahead.
+    f32x16 s[KB];
 #pragma unroll
-      for (int x = 0; x < KB; ++x) s[x] = f32x16{};
-      {
-        constexpr int NS = 2 * KB;
-        i32x8 kr[kPrefK];
+    for (int x = 0; x < KB; ++x) s[x] = f32x16{};
+    {
+      constexpr int NS = 2 * KB;
+      i32x8 kr[kPrefK];
 #pragma unroll
-        for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(kt, lane, 32 * (i % KB), i / KB);
+      for (int i = 0; i < kPrefK; ++i) kr[i] = k_frag(kt, lane, 32 * (i % KB), i / KB);
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const i32x8 a = kr[i % kPrefK];
-          if (i + kPrefK < NS) kr[i % kPrefK] = k_frag(kt, lane, 32 * ((i + kPrefK) % KB), (i + kPrefK) / KB);
-          s[i % KB] = mfma_f8(a, qf[i / KB], s[i % KB]);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefK, 0);
-#pragma unroll
-        for (int i = 0; i < NS - kPrefK; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefK, 0);
+      for (int i = 0; i < NS; ++i) {
+        const i32x8 a = kr[i % kPrefK];
+        if (i + kPrefK < NS) kr[i % kPrefK] = k_frag(kt, lane, 32 * ((i + kPrefK) % KB), (i + kPrefK) / KB);
+        s[i % KB] = mfma_f8(a, qf[i / KB], s[i % KB]);
       }
-
-      const bool need_mask = (kstart + kF8BC > N) || (CAUSAL && kstart + kF8BC - 1 > qw0);
-      if (need_mask) {
-        const int q = qw0 + l32;
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPrefK, 0);
 #pragma unroll
-        for (int x = 0; x < KB; ++x)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kstart + 32 * x + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key >= N || (CAUSAL && key > q)) s[x][i] = -INFINITY;
-          }
+      for (int i = 0; i < NS - kPrefK; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefK, 0);
+    }
 
-      // online softmax (exact running max; key 0 is visible to every row, so
-      // m_run is finite from the first visited tile on)
-      float mx = -INFINITY;
+    if (MASK) {
+      const int q = qw0 + l32;
 #pragma unroll
       for (int x = 0; x < KB; ++x)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[x][i]);
-      mx = pair_max(mx) * scale_log2;
-      const bool move = mx > m_run;
-      if (__any(move)) {
-        const float m_new = move ? mx : m_run;
-        const float alpha = exp2_fast(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-      }
-      // p' = 2^(s - m + 8) in [0, 256]; the sum takes p' before rounding
-      const float shift = 8.f - m_run;
-      i32x8 pf[KB / 2];
-      float lsum = 0.f;
-#pragma unroll
-      for (int y = 0; y < KB / 2; ++y) {
-        int wv[8];
-#pragma unroll
-        for (int xx = 0; xx < 2; ++xx)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float p[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              p[e] = exp2_fast(__builtin_fmaf(s[2 * y + xx][4 * r + e], scale_log2, shift));
-              lsum += p[e];
-            }
-            wv[4 * xx + r] = pack4_f8(p[0], p[1], p[2], p[3]);
-          }
-        pf[y] = i32x8{wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]};
-      }
-      l_run += lsum;
-
-      // O^T[db] += V^T P^T over the tile's two 64-key pairs; step i is pair
-      // i / DB, d block i % DB, with the V^T fragments kPrefV steps ahead
-      {
-        constexpr int NP = (KB / 2) * DB;
-        i32x8 vr[kPrefV];
-#pragma unroll
-        for (int i = 0; i < kPrefV; ++i) vr[i] = vt_frag(vt, lane, 64 * (i / DB), i % DB);
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const i32x8 a = vr[i % kPrefV];
-          if (i + kPrefV < NP) vr[i % kPrefV] = vt_frag(vt, lane, 64 * ((i + kPrefV) / DB), (i + kPrefV) % DB);
-          acc[i % DB] = mfma_f8(a, pf[i / DB], acc[i % DB]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = kstart + 32 * x + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (key >= N || (CAUSAL && key > q)) s[x][i] = -INFINITY;
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPrefV, 0);
-#pragma unroll
-        for (int i = 0; i < NP - kPrefV; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefV, 0);
-      }
     }
+
+    // online softmax (exact running max; key 0 is visible to every row, so
+    // m_run is finite from the first visited tile on)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < KB; ++x)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[x][i]);
+    mx = pair_max(mx) * scale_log2;
+    const bool move = mx > m_run;
+    if (__any(move)) {
+      const float m_new = move ? mx : m_run;
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    // p' = 2^(s - m + 8) in [0, 256]; the sum takes p' before rounding
+    const float shift = 8.f - m_run;
+    i32x8 pf[KB / 2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int y = 0; y < KB / 2; ++y) {
+      int wv[8];
+#pragma unroll
+      for (int xx = 0; xx < 2; ++xx)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = exp2_fast(__builtin_fmaf(s[2 * y + xx][4 * r + e], scale_log2, shift));
+            lsum += p[e];
+          }
+          wv[4 * xx + r] = pack4_f8(p[0], p[1], p[2], p[3]);
+        }
+      pf[y] = i32x8{wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]};
+    }
+    l_run += lsum;
+
+    // O^T[db] += V^T P^T over the tile's two 64-key pairs; step i is pair
+    // i / DB, d block i % DB, with the V^T fragments kPrefV steps ahead
+    {
+      constexpr int NP = (KB / 2) * DB;
+      i32x8 vr[kPrefV];
+#pragma unroll
+      for (int i = 0; i < kPrefV; ++i) vr[i] = vt_frag(vt, lane, 64 * (i / DB), i % DB);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const i32x8 a = vr[i % kPrefV];
+        if (i + kPrefV < NP) vr[i % kPrefV] = vt_frag(vt, lane, 64 * ((i + kPrefV) / DB), (i + kPrefV) % DB);
+        acc[i % DB] = mfma_f8(a, pf[i / DB], acc[i % DB]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4 * kPrefV, 0);
+#pragma unroll
+      for (int i = 0; i < NP - kPrefV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefV, 0);
+    }
+  };
+  int j = 0;
+  for (; j < n_plain; ++j) {
+    if (j + 1 < n_tiles) issue_tile(j + 1);
+    tile(j, std::false_type{});
+    wait_all_memory();
+    __syncthreads();
+  }
+  for (; j < n_act; ++j) {
+    if (j + 1 < n_tiles) issue_tile(j + 1);
+    tile(j, std::true_type{});
+    wait_all_memory();
+    __syncthreads();
+  }
+  for (; j < n_tiles; ++j) {
+    if (j + 1 < n_tiles) issue_tile(j + 1);
     wait_all_memory();
     __syncthreads();
   }
