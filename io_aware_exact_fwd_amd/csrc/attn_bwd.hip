@@ -93,7 +93,8 @@ __device__ __forceinline__ void dkdv_block(
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar tile tests
   const int kg = wave % NWK;      // key group: keys kw0 .. kw0+31
   const int qh = wave / NWK;      // query half: rows 32*qh .. 32*qh+31 of each tile
 
@@ -249,25 +250,30 @@ __device__ __forceinline__ void dkdv_block(
       // P = 2^(s*tau*log2e - LSE*log2e), dS = P (dP - D); rows 8r + 4hi + 0..3
       const bool need_mask = (CAUSAL && qs < kw0 + 31) ||
                              (LOCAL && (qs + 31 > kw0 + window || (!CAUSAL && qs < kw0 + 31 - window)));
-      const int key = kw0 + l32;
       float p[16], ds[16];
+      f32x4 dv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const f32x4 lv = *(const f32x4*)(lse_l + 32 * qh + 8 * r + 4 * hi);
-        const f32x4 dv = *(const f32x4*)(del_l + 32 * qh + 8 * r + 4 * hi);
+        dv[r] = *(const f32x4*)(del_l + 32 * qh + 8 * r + 4 * hi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * r + e;
-          float pv = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lv[e]));
-          if (need_mask) {
-            const int q = qs + 8 * r + 4 * hi + e;
-            if ((CAUSAL && key > q) || (LOCAL && (key < q - window || (!CAUSAL && key > q + window))))
-              pv = 0.f;
-          }
-          p[i] = pv;
-          ds[i] = pv * (dp[i] - dv[e]);
+        for (int e = 0; e < 4; ++e) p[4 * r + e] = exp2_fast(__builtin_fmaf(s[4 * r + e], scale_log2, -lv[e]));
+      }
+      // The mask, as one branch for the tile so that unmasked tiles skip it:
+      // slot 4r + e holds query qs + 4hi + c with c = 8r + e and this lane's
+      // key is kw0 + l32, so with t = kw0 + l32 - qs - 4hi each test is a
+      // compare of the constant c -- key > q <=> c < t, key < q - window <=>
+      // c > t + window, key > q + window <=> c < t - window.
+      if (need_mask) {
+        const int t = kw0 + l32 - qs - 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 8 * (i >> 2) + (i & 3);
+          if ((CAUSAL && c < t) || (LOCAL && (c > t + window || (!CAUSAL && c < t - window)))) p[i] = 0.f;
         }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp[i] - dv[i >> 2][i & 3]);
 
       // dV^T += dO^T P and dK^T += Q^T dS: k slots of slab h2 are query rows
       // 16*h2 + {4hi..4hi+3, 8+4hi..8+4hi+3} of this wave's 32 rows
@@ -470,18 +476,29 @@ __device__ __forceinline__ void dq_block(
           }
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefetch, 0);
         }
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lse_l2));
+        // The mask, as one branch for the block: slot i holds key kb0 + c with
+        // kb0 = kstart + 32x + 4hi and c = 8(i/4) + i%4, so with t = q - kb0
+        // each test is a compare of the constant c -- key >= N <=> c > N - kb0
+        // - 1, key > q <=> c > t, key > q + window <=> c > t + window, key <
+        // q - window <=> c < t - window.
+        if (need_mask) {
+          const int kb0 = kstart + x * 32 + 4 * hi;
+          const int t = q - kb0;
+          int lim = N - kb0 - 1;
+          if (CAUSAL) lim = min(lim, t);
+          if (LOCAL && !CAUSAL) lim = min(lim, t + window);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = 8 * (i >> 2) + (i & 3);
+            if (c > lim || (LOCAL && c < t - window)) p[i] = 0.f;
+          }
+        }
         float ds[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lse_l2));
-          if (need_mask) {
-            const int key = kstart + x * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key >= N || (CAUSAL && key > q) ||
-                (LOCAL && (key < q - window || (!CAUSAL && key > q + window))))
-              pv = 0.f;
-          }
-          ds[i] = pv * (dp[i] - del);
-        }
+        for (int i = 0; i < 16; ++i) ds[i] = p[i] * (dp[i] - del);
         // dQ^T += K^T dS^T: k slots of slab h2 are keys 16*h2 + {4hi.., 8+4hi..}
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
