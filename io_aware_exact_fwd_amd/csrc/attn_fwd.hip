@@ -196,17 +196,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
       // mask: only tiles that cross the diagonal, a band edge or the ragged end
       const bool need_mask = (kstart + BC > N) || (CAUSAL && kstart + BC - 1 > qw0) ||
                              (LOCAL && (kstart < qw1 - window || (!CAUSAL && kstart + BC - 1 > qw0 + window)));
+      // Slot i of block x holds key kb0 + c with kb0 = kstart + 32x + 4hi and
+      // c = 8(i/4) + i%4, so with t = q - kb0 each test compares the constant
+      // c: key >= N <=> c > N - kb0 - 1, key > q <=> c > t, key > q + w <=>
+      // c > t + w, key < q - w <=> c < t - w.
       if (need_mask) {
         const int q = qw0 + l32;
 #pragma unroll
-        for (int x = 0; x < KB; ++x)
+        for (int x = 0; x < KB; ++x) {
+          const int kb0 = kstart + x * 32 + 4 * hi;
+          const int t = q - kb0;
+          int lim = N - kb0 - 1;
+          if (CAUSAL) lim = min(lim, t);
+          if (LOCAL && !CAUSAL) lim = min(lim, t + window);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = kstart + x * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            const bool out = key >= N || (CAUSAL && key > q) ||
-                             (LOCAL && (key < q - window || (!CAUSAL && key > q + window)));
-            if (out) s[x][i] = -INFINITY;
+            const int c = 8 * (i >> 2) + (i & 3);
+            if (c > lim || (LOCAL && c < t - window)) s[x][i] = -INFINITY;
           }
+        }
       }
 
       // online softmax: running max, rescale, exp, running sum, P -> bf16

@@ -206,15 +206,18 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kPrefK, 0);
     }
 
+    // slot i of block x holds key kb0 + 8(i/4) + i%4 (kb0 = kstart + 32x + 4hi):
+    // key >= N or key > q is a compare of that constant offset against lim
     if (MASK) {
       const int q = qw0 + l32;
 #pragma unroll
-      for (int x = 0; x < KB; ++x)
+      for (int x = 0; x < KB; ++x) {
+        const int kb0 = kstart + 32 * x + 4 * hi;
+        const int lim = CAUSAL ? min(N - kb0 - 1, q - kb0) : N - kb0 - 1;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kstart + 32 * x + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (key >= N || (CAUSAL && key > q)) s[x][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) > lim) s[x][i] = -INFINITY;
+      }
     }
 
     // online softmax (exact running max; key 0 is visible to every row, so
