@@ -74,7 +74,10 @@ __device__ __forceinline__ i32x8 vt_frag(const unsigned char* tile, int lane, in
 
 // Four probabilities -> four E4M3 bytes (round to nearest even; 0 <= p <= 256).
 __device__ __forceinline__ int pack4_f8(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the two converts write the low and the high half of w; the bits passed
+  // in as the untouched half (a's) are overwritten by the second, and reusing
+  // a's register saves materialising a constant there
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
