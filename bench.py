@@ -254,9 +254,9 @@ def cpu_baseline(w, x, n_heads):
     }
 
 
-# Secondary forward-only legs: the north-star's own forward configurations,
-# timed after the headline step with the same warm-up and timing rules; they
-# do not enter ``value``.
+# Secondary forward-only legs: the causal forward at N = 8192 (32 heads) and
+# N = 16384 (64 query heads over 8 K/V heads), timed after the headline step
+# with the same warm-up and timing rules; they do not enter ``value``.
 FORWARD_LEGS = (("fwd8k", "fwd-8K"), ("gqa16k", "gqa-16K"))
 
 
