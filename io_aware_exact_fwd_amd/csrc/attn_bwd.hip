@@ -6,12 +6,12 @@
 // probabilities from Q, K and that statistic instead of reading an N x N
 // matrix back, trading one extra multiply for a full HBM round trip.
 //
-// With L = sum(dO * O), P_ij = exp(tau q_i.k_j - LSE_i) on visible keys:
+// With P_ij = exp(tau q_i.k_j - LSE_i) on visible keys:
 //   dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,
 //   dS_ij = P_ij (dP_ij - D_i) with D_i = dO_i . O_i (= sum_k P_ik dP_ik),
 //   dQ_i = tau sum_j dS_ij k_j,   dK_j = tau sum_i dS_ij q_i.
 //
-// Three kernels, in stream order, no atomics (bitwise deterministic):
+// Kernels, no atomics (bitwise deterministic):
 //   bwd_pre   D_i = rowsum(dO_i * O_i)                          (memory bound)
 //   bwd_dkdv  one workgroup per (batch, K/V head, 32*NWK keys): the key block's
 //             K and V stay in LDS; 2*NWK waves = NWK key groups of 32 x two
@@ -21,7 +21,12 @@
 //             atomics; the two halves' partial sums are added through LDS at
 //             the end;
 //   bwd_dq    one workgroup per (batch, query head, 32*NW queries); each wave
-//             owns 32 queries with dQ^T in registers and loops over key tiles.
+//             owns 32 queries with dQ^T in registers and loops over key tiles;
+//   bwd_grads the dK/dV and the dQ workgroups in one launch (what attn_bwd
+//             runs after bwd_pre; the two separate kernels serve the
+//             attn_bwd_dkdv and attn_bwd_dq calls, bitwise the same gradients).
+// Causal and window masks are evaluated only on tiles that cross the
+// diagonal, a band edge or the ragged end, as one branch per tile.
 // All tiles move global -> LDS by 16-byte direct loads into the swizzled
 // layout of attn_layout.h; operands are row fragments or transposing LDS
 // reads.  The C layout of one product goes straight back as the B operand of
