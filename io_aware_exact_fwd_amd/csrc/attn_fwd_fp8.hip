@@ -9,10 +9,11 @@
 // LSE in fp32 as in the bf16 forward (page "6.1 …", §2.2).
 //
 // gfx950 mapping (d = 128; the structure of the bf16 forward in attn_fwd.hip):
-//   * one workgroup = 8 waves x 32 query rows of one (b, h), heaviest causal
-//     blocks first; 128-key K and V tiles of 16 KB each, double-buffered
-//     through direct 16-byte global -> LDS loads (an 8-bit row of 128 bytes
-//     has the layout of a d = 64 bf16 row, see attn_layout.h);
+//   * one workgroup = 8 (or, on small grids, 4) waves x 32 query rows of one
+//     (b, h), heaviest causal blocks first; 128-key K and V tiles of 16 KB
+//     each, double-buffered through direct 16-byte global -> LDS loads (an
+//     8-bit row of 128 bytes has the layout of a d = 64 bf16 row, see
+//     attn_layout.h);
 //   * S^T = K Q^T per 32-key block: two 32x32x64 8-bit MFMAs (d 0..63 and
 //     64..127), Q^T held in registers, K row fragments from LDS;
 //   * online softmax in fp32 exactly as the bf16 forward; the probabilities
@@ -40,8 +41,11 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kF8D = 128;       // head dim (bytes per 8-bit row)
 constexpr int kF8BC = 128;      // keys per tile
-constexpr int kF8NW = 8;        // waves per workgroup
-constexpr int kF8BR = kF8NW * 32;
+// Workgroups of 8 waves (256 query rows), or of 4 (128 rows) when 8-wave
+// blocks would leave CUs idle; two waves per SIMD either way (4-wave
+// workgroups run two to a CU).  A wave's work -- its 32 rows against the
+// same 128-key tiles -- is the same in both, so are its outputs, bitwise.
+constexpr int kF8CUs = 256;     // MI355X
 constexpr int kF8Tile = kF8BC * kF8D;           // bytes of one K or V tile
 constexpr int kF8Lds = 2 * 2 * kF8Tile;         // double-buffered K and V (64 KB)
 constexpr int kE8M0One = 127;                   // block scale exponent 0 (x1.0)
@@ -81,8 +85,8 @@ __device__ __forceinline__ int pack4_f8(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
+template <bool CAUSAL, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(2, 2))) void attn_fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ q_descale, const float* __restrict__ k_descale,
@@ -128,7 +132,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
   else if (!(qk > 0.f) || !(scale_log2 < INFINITY)) scale_log2 = __builtin_nanf("");
   const float vds = v_descale[b * Hkv + hk];
 
-  const int q0 = qb * kF8BR;
+  const int q0 = qb * NW * 32;
   const int qw0 = q0 + wave * 32, qw1 = qw0 + 31;
   const bool wave_live = qw0 < N;
 
@@ -146,11 +150,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
 #pragma unroll
   for (int m = 0; m < 2; ++m) asm volatile("" ::"v"(qf[m]));
 
-  const int kv_end = CAUSAL ? min(N, q0 + kF8BR) : N;
+  const int kv_end = CAUSAL ? min(N, q0 + NW * 32) : N;
   const int n_tiles = (kv_end + kF8BC - 1) / kF8BC;
 
   // an 8-bit row of 128 bytes is loaded exactly like a d = 64 bf16 row
-  TileLoader<64, kF8BC, kF8NW> ldr;
+  TileLoader<64, kF8BC, NW> ldr;
   ldr.init(wave, lane);
   auto stage = [&](int j) { return smem + (j & 1) * 2 * kF8Tile; };
   auto issue_tile = [&](int j) {
@@ -323,21 +327,33 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kF8NW * 64, kF8NW * 64),
   }
 }
 
-template <bool CAUSAL>
-hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t stream) {
-  const int n_qb = (a.N + kF8BR - 1) / kF8BR;
+template <bool CAUSAL, int NW>
+hipError_t launch_fp8_nw(const Fp8FwdArgs& a, hipStream_t stream) {
+  const int n_qb = (a.N + NW * 32 - 1) / (NW * 32);
   const int BH = a.B * a.Hq;
   const long long grid = (long long)BH * n_qb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  auto kern = attn_fwd_fp8_kernel<CAUSAL>;
+  auto kern = attn_fwd_fp8_kernel<CAUSAL, NW>;
   static std::atomic<uint64_t> lds_set{0};
   const hipError_t attr = allow_lds_on_device((const void*)kern, kF8Lds, lds_set);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kF8NW * 64), kF8Lds, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), kF8Lds, stream,
                      (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_descale,
                      a.k_descale, a.v_descale, (uint16_t*)a.o, a.lse, a.N, BH, a.Hq, a.Hkv,
                      a.Hq / a.Hkv, n_qb, a.scale * kLog2e, xcd_remap(BH, Packing{}));
   return hipGetLastError();
+}
+
+// 4-wave workgroups when the 8-wave grid has fewer workgroups than CUs, or,
+// under the causal mask, no more than one per CU (the heaviest block then
+// sets the time, and halving the blocks halves it): measured same-process,
+// 25-42 % faster there, while from two 8-wave blocks per CU on the two
+// forms are within a few percent and the 8-wave one is kept.
+template <bool CAUSAL>
+hipError_t launch_fp8_t(const Fp8FwdArgs& a, hipStream_t stream) {
+  const long long grid8 = (long long)a.B * a.Hq * ((a.N + 255) / 256);
+  const bool small = grid8 < kF8CUs || (CAUSAL && grid8 <= kF8CUs);
+  return small ? launch_fp8_nw<CAUSAL, 4>(a, stream) : launch_fp8_nw<CAUSAL, 8>(a, stream);
 }
 
 }  // namespace

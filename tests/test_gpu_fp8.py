@@ -117,6 +117,22 @@ def test_fp8_deterministic(gpu_lib):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("causal,heads", [(True, 16), (False, 8)], ids=["causal", "full"])
+def test_fp8_workgroup_sizes_agree_bitwise(gpu_lib, causal, heads):
+    """The launch takes 4-wave workgroups when 8-wave ones would not fill the
+    chip (causal: at most one 8-wave block per CU; otherwise: fewer than one)
+    and 8-wave ones above that; a wave's work is the same in both.  Heads are
+    independent, so the first half of the heads of an N = 8192 problem (a
+    4-wave launch) must give bitwise the outputs the whole problem (an 8-wave
+    launch) gives for them."""
+    say(f"fp8 4-wave vs 8-wave workgroups causal={causal}")
+    x = make_fp8_inputs(1, heads, heads, 8192, 128, seed=47)
+    half = {n: x[n][:, : heads // 2].copy() for n in ("q8", "k8", "v8", "q_descale", "k_descale", "v_descale")}
+    o_all, lse_all = run(gpu_lib, x, causal)
+    o_half, lse_half = run(gpu_lib, half, causal)
+    assert torch.equal(o_all[:, : heads // 2], o_half) and torch.equal(lse_all[:, : heads // 2], lse_half)
+
+
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_fp8_zero_descales(gpu_lib, causal):
     """A zero descale is an all-zero head: zero queries (uniform attention over
