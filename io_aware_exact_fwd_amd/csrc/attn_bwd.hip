@@ -486,9 +486,9 @@ __device__ __forceinline__ void dq_block(
         for (int i = 0; i < 16; ++i) p[i] = exp2_fast(__builtin_fmaf(s[i], scale_log2, -lse_l2));
         // The mask, as one branch for the block: slot i holds key kb0 + c with
         // kb0 = kstart + 32x + 4hi and c = 8(i/4) + i%4, so with t = q - kb0
-        // each test is a compare of the constant c -- key >= N <=> c > N - kb0
-        // - 1, key > q <=> c > t, key > q + window <=> c > t + window, key <
-        // q - window <=> c < t - window.
+        // each test is a compare of the constant c:
+        //   key >= N <=> c > N - kb0 - 1,   key > q <=> c > t,
+        //   key > q + window <=> c > t + window,   key < q - window <=> c < t - window.
         if (need_mask) {
           const int kb0 = kstart + x * 32 + 4 * hi;
           const int t = q - kb0;
