@@ -87,9 +87,13 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for this problem: O(B*Hq*N), never
- * O(N^2) ([EVOL] §4: memory goes from O(N^2) to O(N)).  Returns 0 when the
- * arguments are invalid.
+ * Bytes of device workspace attn_bwd and attn_bwd_window need for this
+ * problem: linear in N, never O(N^2) ([EVOL] §4: memory goes from O(N^2) to
+ * O(N)).  It holds D = rowsum(dO * O), one fp32 per query row (B*Hq*N*4 bytes,
+ * rounded up to a multiple of 256), and, when Hq > Hkv and the library shares
+ * the Hq/Hkv query heads of each K/V head out over S workgroups, their fp32
+ * partial dK and dV (S*2*B*Hkv*N*d*4 more bytes).  Returns 0 when the arguments
+ * are invalid.
  */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 
@@ -106,7 +110,9 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
  *   workspace  device buffer of workspace_bytes >= attn_bwd_workspace_bytes();
  *              its contents on entry are ignored and on exit are unspecified.
  * Outputs must not alias inputs or each other.  Deterministic: the same
- * inputs give bitwise the same outputs.
+ * inputs give bitwise the same outputs.  With the head split (workspace bytes
+ * beyond the rounded B*Hq*N*4), dK and dV are the fp32 per-split sums added in
+ * split order, then rounded to bf16.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -116,8 +122,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * The stages of attn_bwd, for callers that schedule them themselves.  attn_bwd
- * is attn_bwd_preprocess followed by attn_bwd_grads; attn_bwd_grads computes
- * bitwise what attn_bwd_dkdv and attn_bwd_dq compute, in one launch.  The
+ * is attn_bwd_preprocess followed by attn_bwd_grads, bitwise, whenever
+ * attn_bwd_workspace_bytes is the rounded B*Hq*N*4 (no head split); otherwise
+ * dQ is still bitwise equal, and dK and dV, which the stages sum over all
+ * query heads in one workgroup, differ from attn_bwd's by fp32 rounding of the
+ * summation order (at most about one bf16 unit in the last place).
+ * attn_bwd_grads computes bitwise what attn_bwd_dkdv and attn_bwd_dq compute,
+ * in one launch.  The
  * gradient stages read only the inputs, the LSE and delta, so they may run on
  * different streams once delta is written.  Same conventions and errors as
  * attn_bwd.

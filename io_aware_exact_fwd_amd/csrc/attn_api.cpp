@@ -103,11 +103,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* o, const f
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_UNSUPPORTED;
-  if (workspace_bytes < attn::bwd_workspace_bytes(B, Hq, N)) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < attn::bwd_workspace_bytes(B, Hq, Hkv, N, d)) return ATTN_ERR_WORKSPACE;
   if ((rc = check_scale(scale))) return rc;
   if ((rc = current_device_check())) return rc;
   attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace,
                   B, Hq, Hkv, N, d, causal != 0, scale, window};
+  // the head split's partial sums follow D in the workspace
+  a.kv_splits = attn::bwd_kv_splits(B, Hq, Hkv, N, causal != 0, window);
+  a.part = (float*)((char*)workspace + attn::bwd_delta_bytes(B, Hq, N));
   hipError_t e = attn::launch_bwd(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, where);
 }
@@ -131,7 +134,7 @@ ATTN_EXPORT int attn_fwd_window(const void* q, const void* k, const void* v, voi
 
 ATTN_EXPORT size_t attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   if (check_problem(B, Hq, Hkv, N, d)) return 0;
-  return attn::bwd_workspace_bytes(B, Hq, N);
+  return attn::bwd_workspace_bytes(B, Hq, Hkv, N, d);
 }
 
 ATTN_EXPORT int attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -83,14 +83,17 @@ struct DkdvCfg {
 };
 
 // One dK/dV workgroup: w is its index in the dK/dV grid, smem its LDS.  With
-// LOCAL, query i sees key j only when |i - j| <= window.
+// LOCAL, query i sees key j only when |i - j| <= window.  With S > 1 (fixed
+// length only) the G query heads of each K/V head are shared out over S
+// workgroups of G/S heads each, which write fp32 partial sums to `part`
+// instead of dK and dV.
 template <int D, int NWK, bool CAUSAL, bool LOCAL>
 __device__ __forceinline__ void dkdv_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int Nmax, int BHkv, int Hq, int Hkv, int G,
-    float scale, float scale_log2, int xcd_remap, int window, const Packing& pk, int w,
-    unsigned char* smem) {
+    float scale, float scale_log2, int xcd_remap, int window, const Packing& pk, int w, int S,
+    float* __restrict__ part, unsigned char* smem) {
   using C = DkdvCfg<D, NWK>;
   constexpr int kPrefetch = 3;   // (A, B) fragment pairs in flight ahead of their MFMA
   constexpr int NW = C::kNW;
@@ -104,9 +107,9 @@ __device__ __forceinline__ void dkdv_block(
   const int qh = wave / NWK;      // query half: rows 32*qh .. 32*qh+31 of each tile
 
   // heaviest key blocks (the first ones under the causal mask) first; when
-  // B*Hkv is a multiple of 8 all key blocks of one K/V head share an XCD, so
-  // the Q/dO tiles they all read stay in that XCD's L2
-  int b, hk, kb;
+  // B*Hkv*S is a multiple of 8 all key blocks of one (K/V head, split) share
+  // an XCD, so the Q/dO tiles they all read stay in that XCD's L2
+  int b, hk, kb, split = 0;
   if (pk.cu && BHkv / Hkv <= kMaxPackedSeqs) {
     // packed: real key blocks only, heaviest (most query tiles after them) first
     PackedUnits pu;
@@ -116,27 +119,31 @@ __device__ __forceinline__ void dkdv_block(
     const int len = seq_span(pk, Nmax, b).len;
     kb = (len + C::kBKV - 1) / C::kBKV - 1 - level;
   } else {
-    int bhk;
+    const int BHS = BHkv * S;   // (K/V head, split) pairs
+    int bhs;
     if (xcd_remap) {
-      const int hx = BHkv >> 3;
+      const int hx = BHS >> 3;
       const int i = w >> 3;
-      bhk = (w & 7) * hx + (i % hx);
+      bhs = (w & 7) * hx + (i % hx);
       kb = i / hx;
     } else {
-      bhk = w % BHkv;
-      kb = w / BHkv;
+      bhs = w % BHS;
+      kb = w / BHS;
     }
+    const int bhk = bhs / S;
+    split = bhs - bhk * S;
     b = bhk / Hkv;
     hk = bhk - b * Hkv;
   }
+  const int Gs = G / S;                  // query heads of this workgroup
   const SeqSpan sp = seq_span(pk, Nmax, b);
   const int N = sp.len;                  // rows of this sequence
   const int k0 = kb * C::kBKV;
   if (k0 >= N) return;                   // a block past a shorter packed sequence (uniform)
   const int kw0 = k0 + kg * 32;
   const size_t kv_off = sp.row0(pk, Nmax, b, hk, Hkv) * D;
-  // rows of query head hk*G + hh start at q_row0 + hh * q_hstride
-  const size_t q_row0 = sp.row0(pk, Nmax, b, hk * G, Hq);
+  // rows of query head hk*G + split*Gs + hh start at q_row0 + hh * q_hstride
+  const size_t q_row0 = sp.row0(pk, Nmax, b, hk * G + split * Gs, Hq);
   const size_t q_hstride = head_stride(pk, Nmax);
 
   unsigned char* Kt = smem + C::kK;
@@ -150,9 +157,9 @@ __device__ __forceinline__ void dkdv_block(
   const int qt0 = q_first / BQ;
   const int qt_end = LOCAL ? min(n_qt, (k0 + C::kBKV + window + BQ - 1) / BQ) : n_qt;
   const int per_head = qt_end - qt0;
-  const int n_iter = per_head * G;
+  const int n_iter = per_head * Gs;
 
-  // the query tile of iteration it is (head hk*G + it / per_head, tile
+  // the query tile of iteration it is (head hk*G + split*Gs + it / per_head, tile
   // qt0 + it % per_head); both are stepped incrementally instead of divided
   TileLoader<D, BQ, NW> ldq;
   ldq.init(wave, lane);
@@ -316,7 +323,26 @@ __device__ __forceinline__ void dkdv_block(
 
   // epilogue: lane holds key kw0 + l%32, d rows db*32 + 8r + 4hi + 0..3
   const int key = kw0 + l32;
-  if (key < N) {
+  if (key < N && part) {
+    // this split's fp32 sums, dK still unscaled
+    const size_t plane = (size_t)BHkv * Nmax * D;
+    float* pkr = part + 2 * split * plane + kv_off + (size_t)key * D;
+    float* pvr = pkr + plane;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = db * 32 + 8 * r + 4 * hi;
+        f32x4 a, v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = dkT[db][4 * r + e] + *red_at(0, db, 4 * r + e);
+          v[e] = dvT[db][4 * r + e] + *red_at(1, db, 4 * r + e);
+        }
+        *(f32x4*)(pkr + d0) = a;
+        *(f32x4*)(pvr + d0) = v;
+      }
+  } else if (key < N) {
     uint16_t* dkr = dK + kv_off + (size_t)key * D;
     uint16_t* dvr = dV + kv_off + (size_t)key * D;
 #pragma unroll
@@ -346,7 +372,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(2 * NWK * 64, 2 * NWK * 64
     float scale, float scale_log2, int xcd_remap, int window, Packing pk) {
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
-                                    scale_log2, xcd_remap, window, pk, blockIdx.x, smem);
+                                    scale_log2, xcd_remap, window, pk, blockIdx.x, 1, nullptr,
+                                    smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -548,7 +575,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 // dK/dV units, then its real dQ units, then empty workgroups).  The two
 // halves are independent (both read only the inputs, LSE and D), so dQ blocks
 // fill the CUs that dK/dV blocks release instead of waiting for the whole
-// dK/dV grid to drain.  Both halves use 8 waves.
+// dK/dV grid to drain.  Both halves use 8 waves.  With S > 1 the dK/dV blocks
+// write partial sums to `part` (see dkdv_block) for bwd_dkdv_reduce_kernel.
 template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(WPE, WPE))) void bwd_grads_kernel(
@@ -556,7 +584,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dl,
     uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
     int BHkv, int BH, int Hq, int Hkv, int G, int n_dkdv, int n_qb, float scale, float scale_log2,
-    int xcd_kv, int xcd_q, int window, Packing pk) {
+    int xcd_kv, int xcd_q, int window, Packing pk, int S, float* __restrict__ part) {
   static_assert(2 * NWK == NW, "both halves run the same number of waves");
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   const int w = blockIdx.x;
@@ -570,10 +598,30 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
   }
   if (w < split)
     dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
-                                      scale_log2, xcd_kv, window, pk, w, smem);
+                                      scale_log2, xcd_kv, window, pk, w, S, part, smem);
   else
     dq_block<D, BC, NW, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dQ, N, BH, Hq, Hkv, G, n_qb, scale,
                                        scale_log2, xcd_q, window, pk, w - split, smem);
+}
+
+// dK = scale * sum_s part[s][0], dV = sum_s part[s][1], added in split order
+// (so the result is the same on every run), rounded to bf16.  Thread i takes
+// elements 4i .. 4i+3 of the n4 * 4 in each plane.
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
+                                                              uint16_t* __restrict__ dK,
+                                                              uint16_t* __restrict__ dV,
+                                                              size_t n4, int S, float scale) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* p = (const f32x4*)part + i;
+  f32x4 k = p[0], v = p[n4];
+  for (int s = 1; s < S; ++s) {
+    k += p[2 * s * n4];
+    v += p[(2 * s + 1) * n4];
+  }
+  *(u32x2*)(dK + 4 * i) = u32x2{pack_bf16x2(k[0] * scale, k[1] * scale),
+                                pack_bf16x2(k[2] * scale, k[3] * scale)};
+  *(u32x2*)(dV + 4 * i) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // Dynamic LDS beyond 64 KB, allowed once per kernel instance and device.
@@ -593,6 +641,9 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
 
 // dK/dV: 4 key groups x 2 query halves = 8 waves, 128 keys per workgroup.
 constexpr int kDkdvNWK = 4, kDkdvWPE = 2;
+// Packed batches keep one workgroup per key block.
+inline int kv_splits_of(const BwdArgs& a) { return a.pack.cu ? 1 : a.kv_splits; }
+static_assert(kDkdvNWK * 32 == kBwdKeysPerBlock, "the host's split rule counts these blocks");
 // dQ: 8 waves x 32 queries, 128-key tiles (128 KB of double-buffered LDS).
 constexpr int kDqBC = 128, kDqNW = 8, kDqWPE = 2;
 
@@ -654,7 +705,8 @@ struct LaunchGrads {
     const int BHkv = a.B * a.Hkv, BH = a.B * a.Hq;
     const int n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
     const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
-    const long long n_dkdv = (long long)BHkv * n_kb;
+    const int S = kv_splits_of(a);
+    const long long n_dkdv = (long long)BHkv * n_kb * S;
     const long long grid = packed_grid(a.pack, a.B, a.Hkv, CK::kBKV, n_dkdv) +
                            packed_grid(a.pack, a.B, a.Hq, CQ::kBQ, (long long)BH * n_qb);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -663,8 +715,8 @@ struct LaunchGrads {
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (uint16_t*)a.dk,
                        (uint16_t*)a.dv, a.N, BHkv, BH, a.Hq, a.Hkv, a.Hq / a.Hkv, (int)n_dkdv,
-                       n_qb, a.scale, a.scale * kLog2e, xcd_remap(BHkv, a.pack),
-                       xcd_remap(BH, a.pack), a.window, a.pack);
+                       n_qb, a.scale, a.scale * kLog2e, xcd_remap(BHkv * S, a.pack),
+                       xcd_remap(BH, a.pack), a.window, a.pack, S, S > 1 ? a.part : nullptr);
     return hipGetLastError();
   }
 };
@@ -685,7 +737,14 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream) {
-  return dispatch<LaunchGrads>(a, stream);
+  const int S = kv_splits_of(a);
+  if (S < 1 || (a.Hq / a.Hkv) % S != 0 || (S > 1 && !a.part)) return hipErrorInvalidValue;
+  hipError_t e = dispatch<LaunchGrads>(a, stream);
+  if (e != hipSuccess || S == 1) return e;
+  const size_t n4 = (size_t)a.B * a.Hkv * a.N * a.d / 4;
+  hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
+                     stream, a.part, (uint16_t*)a.dk, (uint16_t*)a.dv, n4, S, a.scale);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream) {

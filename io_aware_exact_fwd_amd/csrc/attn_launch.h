@@ -86,13 +86,68 @@ struct BwdArgs {
   float scale;
   int window = -1;  // sliding window: keys with |i - j| <= window; < 0 = none
   Packing pack;
+  // dK/dV head split: the Hq/Hkv query heads of a K/V head are shared out
+  // over kv_splits workgroups per key block, each writing fp32 partial sums
+  // [kv_splits, 2 (dK unscaled, dV), B*Hkv*N, d] to `part`; a reduction adds
+  // them in split order.  1 = one workgroup sums all heads and writes bf16.
+  int kv_splits = 1;
+  float* part = nullptr;
   // query rows over all heads: B*Hq*N, or Hq*T when packed
   size_t rows() const { return pack.cu ? (size_t)Hq * pack.T : (size_t)B * Hq * N; }
 };
 
-// Bytes of workspace the backward uses (fp32 D per query row).
-inline size_t bwd_workspace_bytes(int B, int Hq, int N) {
-  return (size_t)B * Hq * N * sizeof(float);
+// Keys per dK/dV workgroup of the backward.
+constexpr int kBwdKeysPerBlock = 128;
+
+// dK/dV head splits for a fixed-length problem.  Each dK/dV workgroup sums
+// over all G = Hq/Hkv query heads of its K/V head, so with few K/V heads the
+// U = B*Hkv*ceil(N/128) workgroups are too few to fill 256 CUs, or their
+// longest outlast the rest of the launch.  Splitting the heads S ways makes
+// S*U workgroups of 1/S the work, at the price of 16*d bytes of fp32 partial
+// sums written and read back per key row, K/V head and split.
+//  - Causal, no window: block sizes fall linearly (heaviest first), and the
+//    idle tail of the launch is about a fifth of the work times 256 / (S*U).
+//    Against the partials' traffic (both grow as N*d) that is least at
+//    S^2 = 16 G / (B*Hkv), whatever N and d: S is the largest divisor of G
+//    with S^2 * B*Hkv <= 16 G.
+//  - Otherwise every block carries the same work and one full wave of
+//    blocks suffices: the smallest divisor of G with S*U >= 256.
+inline int bwd_kv_splits(int B, int Hq, int Hkv, int N, bool causal, int window) {
+  const int G = Hq / Hkv;
+  if (G < 2) return 1;
+  const long long bh = (long long)B * Hkv;
+  const long long units = bh * ((N + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock);
+  const bool local = window >= 0 && window < N - 1;
+  int S = 1;
+  if (causal && !local) {
+    for (int s = 2; s <= G; ++s)
+      if (G % s == 0 && (long long)s * s * bh <= 16LL * G) S = s;
+  } else {
+    for (S = 1; S < G && units * S < 256;)
+      do ++S; while (G % S != 0);
+  }
+  return S;
+}
+
+// The most splits any mask takes for this shape: the workspace holds that many.
+inline int bwd_kv_splits_max(int B, int Hq, int Hkv, int N) {
+  const int a = bwd_kv_splits(B, Hq, Hkv, N, true, -1);
+  const int b = bwd_kv_splits(B, Hq, Hkv, N, false, -1);
+  return a > b ? a : b;
+}
+
+// Bytes of the fp32 D rows at the head of the backward's workspace, rounded
+// up so that the partial sums after them start 256-byte aligned.
+inline size_t bwd_delta_bytes(int B, int Hq, int N) {
+  return ((size_t)B * Hq * N * sizeof(float) + 255) & ~(size_t)255;
+}
+
+// Bytes of workspace the backward uses: fp32 D per query row, then the head
+// split's partial sums (2 fp32 d-vectors per key row and split).
+inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  const int S = bwd_kv_splits_max(B, Hq, Hkv, N);
+  const size_t part = S > 1 ? (size_t)S * 2 * B * Hkv * N * d * sizeof(float) : 0;
+  return bwd_delta_bytes(B, Hq, N) + part;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -146,8 +201,10 @@ constexpr size_t kDecodeStaticScratchBytes = size_t{32} << 20;
 // decode launch writes each partial it later reads.
 hipError_t decode_static_scratch(float** out);
 // The backward's stages.  Each reads the BwdArgs fields it needs (delta must
-// be set for all of them).  launch_bwd_grads runs dK/dV and dQ in one launch;
-// launch_bwd is launch_bwd_pre followed by launch_bwd_grads.
+// be set for all of them).  launch_bwd_grads runs dK/dV and dQ in one launch,
+// followed by the reduction of the partial sums when kv_splits > 1 (fixed
+// length only; launch_bwd_dkdv ignores kv_splits); launch_bwd is
+// launch_bwd_pre followed by launch_bwd_grads.
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);

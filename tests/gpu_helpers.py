@@ -81,3 +81,20 @@ def rel_maxnorm(a: torch.Tensor, b: torch.Tensor, floor: float = 0.0) -> float:
     den = max(float(b.abs().max()), floor, 1e-30)
     _log("rel", a, b, den)
     return float((a - b).abs().max() / den)
+
+
+def bwd_head_split(attn, B: int, Hq: int, Hkv: int, N: int, d: int) -> bool:
+    """Whether attn_bwd shares each K/V head's query heads out over several
+    workgroups for this shape: its workspace then holds partial sums beyond the
+    one fp32 D per query row (rounded up to 256 bytes)."""
+    delta = (B * Hq * N * 4 + 255) // 256 * 256
+    return attn.bwd_workspace_bytes(B, Hq, Hkv, N, d) > delta
+
+
+def assert_same_sum_to_bf16_ulp(a: torch.Tensor, b: torch.Tensor) -> None:
+    """a and b are bf16 roundings of one fp32 sum taken in two orders: each
+    element may differ by one bf16 unit in the last place (at most 2^-7 of its
+    magnitude), plus fp32 reassociation error (floored at 1e-4 of max |b|)."""
+    x, y = a.float(), b.float()
+    bound = 2.0 ** -7 * torch.maximum(x.abs(), y.abs()) + 1e-4 * float(y.abs().max())
+    assert bool(((x - y).abs() <= bound).all()), float(((x - y).abs() - bound).max())

@@ -102,11 +102,17 @@ def test_bwd_null(L, which):
 
 
 def test_bwd_workspace(L):
+    # one fp32 D per query row, rounded up to 256 bytes: O(N), not O(N^2)
+    assert L.attn_bwd_workspace_bytes(1, 8, 8, 32768, 128) == 8 * 32768 * 4
+    assert L.attn_bwd_workspace_bytes(1, 3, 3, 10, 64) == 256
+    assert L.attn_bwd_workspace_bytes(4, 8, 4, 2048, 128) == 4 * 8 * 2048 * 4
+    # with the head split, S fp32 partial dK and dV per key row after D:
+    # 32 query heads over 1 K/V head split 16 ways, 8 over 2 (B=2) 4 ways
+    assert L.attn_bwd_workspace_bytes(1, 32, 1, 8192, 128) == 32 * 8192 * 4 + 16 * 2 * 8192 * 128 * 4
     need = L.attn_bwd_workspace_bytes(2, 8, 2, 1000, 128)
-    assert need == 2 * 8 * 1000 * 4           # one fp32 per query row: O(N), not O(N^2)
+    assert need == 2 * 8 * 1000 * 4 + 4 * 2 * (2 * 2 * 1000) * 128 * 4
     assert bwd(L, B=2, Hq=8, Hkv=2, N=1000, d=128, ws_bytes=need - 1) == 4
     assert L.attn_bwd_workspace_bytes(1, 3, 2, 10, 64) == 0      # invalid problem -> 0
-    assert L.attn_bwd_workspace_bytes(1, 8, 8, 32768, 128) == 8 * 32768 * 4
 
 
 def test_bwd_shape_and_scale(L):

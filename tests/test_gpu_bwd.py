@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL_GRAD_REL, TOL_LSE, TOL_O, dev_f64, max_abs, rel_maxnorm, say, to_dev, to_f64
+from gpu_helpers import (TOL_GRAD_REL, TOL_LSE, TOL_O, assert_same_sum_to_bf16_ulp, bwd_head_split, dev_f64,
+                         max_abs, rel_maxnorm, say, to_dev, to_f64)
 from oracle import attention_backward, attention_forward
 from synth_inputs import make_custom_inputs, make_inputs
 
@@ -114,13 +115,50 @@ def test_bwd_fb_32k_full(gpu_lib):
     assert max(rel.values()) <= TOL_GRAD_REL, rel
 
 
-def test_bwd_deterministic(gpu_lib):
-    say("bwd determinism")
-    x = make_custom_inputs(1, 8, 2, 1200, 128, seed=14, with_grad=True)
+@pytest.mark.parametrize("shape", [(1, 8, 2, 1200, 128), (4, 8, 8, 1200, 128)], ids=["split", "plain"])
+def test_bwd_deterministic(gpu_lib, shape):
+    """Bitwise run-to-run determinism, with and without the head split."""
+    say(f"bwd determinism {shape}")
+    assert bwd_head_split(gpu_lib, *shape) == (shape[1] != shape[2])
+    x = make_custom_inputs(*shape, seed=14, with_grad=True)
     a = run_fwd_bwd(gpu_lib, x, True)
     b = run_fwd_bwd(gpu_lib, x, True)
     for t1, t2 in zip(a, b):
         assert torch.equal(t1, t2)
+
+
+# Shapes whose backward shares each K/V head's query heads out over several
+# workgroups (fp32 partial dK/dV in the workspace, added by a reduction):
+# multi-query with many heads, grouped heads with a ragged last key block,
+# d = 64, a batch.
+HEAD_SPLIT = [
+    # B, Hq, Hkv, N, d
+    (1, 16, 1, 1000, 128),
+    (1, 12, 2, 777, 64),
+    (2, 8, 2, 300, 128),
+    (1, 6, 3, 129, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("shape", HEAD_SPLIT, ids=lambda s: "B{}_Hq{}_Hkv{}_N{}_d{}".format(*s))
+def test_bwd_head_split(gpu_lib, shape, causal):
+    say(f"bwd head split {shape} causal={causal}")
+    assert bwd_head_split(gpu_lib, *shape)
+    x = make_custom_inputs(*shape, seed=1700 + shape[3] + shape[1], with_grad=True)
+    check_grads(gpu_lib, x, causal, label=f"split {shape}")
+
+
+@pytest.mark.timeout(600)
+def test_bwd_head_split_mqa_4k(gpu_lib):
+    """Multi-query at its working size: 32 query heads over one K/V head,
+    N = 4096, causal -- the backward splits the heads 16 ways (512 dK/dV
+    workgroups); every element of dQ, dK, dV against the oracle."""
+    shape = (1, 32, 1, 4096, 128)
+    say(f"bwd head split mqa {shape}")
+    assert bwd_head_split(gpu_lib, *shape)
+    x = make_custom_inputs(*shape, seed=1750, with_grad=True)
+    check_grads(gpu_lib, x, True, label="mqa 32/1 4K")
 
 
 def test_bwd_workspace_errors(gpu_lib):
@@ -135,10 +173,16 @@ def test_bwd_workspace_errors(gpu_lib):
 
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-def test_bwd_stages_equal_bwd(gpu_lib, causal):
-    """preprocess -> dkdv -> dq and preprocess -> grads give bitwise what attn_bwd gives."""
-    say(f"bwd stages causal={causal}")
-    x = make_custom_inputs(2, 6, 2, 700, 128, seed=16, with_grad=True)
+@pytest.mark.parametrize("shape,split", [((4, 8, 4, 2048, 128), False), ((2, 6, 2, 700, 128), True)],
+                         ids=["plain", "split"])
+def test_bwd_stages_equal_bwd(gpu_lib, shape, split, causal):
+    """preprocess -> dkdv -> dq and preprocess -> grads give what attn_bwd
+    gives: bitwise without the head split; with it, dQ bitwise and dK, dV (one
+    fp32 sum over the query heads in the stages, per-split sums added in split
+    order in attn_bwd) to one bf16 unit in the last place."""
+    say(f"bwd stages {shape} causal={causal}")
+    assert bwd_head_split(gpu_lib, *shape) == split
+    x = make_custom_inputs(*shape, seed=16, with_grad=True)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = gpu_lib.fwd(q, k, v, causal=causal)
     dq, dk, dv = gpu_lib.bwd(q, k, v, o, lse, do, causal=causal)
@@ -147,8 +191,13 @@ def test_bwd_stages_equal_bwd(gpu_lib, causal):
     dq2 = gpu_lib.bwd_dq(q, k, v, do, lse, delta, causal=causal)
     dq3, dk3, dv3 = gpu_lib.bwd_grads(q, k, v, do, lse, delta, causal=causal)
     torch.cuda.synchronize()
-    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
-    assert torch.equal(dq, dq3) and torch.equal(dk, dk3) and torch.equal(dv, dv3)
+    assert torch.equal(dq, dq2) and torch.equal(dq, dq3)
+    assert torch.equal(dk2, dk3) and torch.equal(dv2, dv3)
+    if split:
+        assert_same_sum_to_bf16_ulp(dk, dk2)
+        assert_same_sum_to_bf16_ulp(dv, dv2)
+    else:
+        assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
     # delta is the softmax-Jacobian row term: rowsum(dO * O) of the bf16 tensors
     ref = (do.float() * o.float()).sum(-1)
     assert float((delta - ref).abs().max()) <= 1e-4 * float(ref.abs().max())

@@ -12,7 +12,8 @@ band, and windows that cover every key (the plain kernels, bitwise).
 import pytest
 import torch
 
-from gpu_helpers import TOL_GRAD_REL, TOL_LSE, TOL_O, dev_f64, max_abs, rel_maxnorm, say, to_dev, to_f64
+from gpu_helpers import (TOL_GRAD_REL, TOL_LSE, TOL_O, assert_same_sum_to_bf16_ulp, bwd_head_split, dev_f64,
+                         max_abs, rel_maxnorm, say, to_dev, to_f64)
 from oracle import attention_backward, attention_forward, backward_dq_rows, forward_rows
 from synth_inputs import make_custom_inputs
 
@@ -91,10 +92,15 @@ def test_window_covering_every_key_is_the_plain_call(gpu_lib, causal):
             assert torch.equal(a, b)
 
 
-def test_window_deterministic_and_stages(gpu_lib):
-    """Bitwise run-to-run determinism; preprocess + grads_window equals bwd_window."""
-    say("window determinism and stages")
-    x = make_custom_inputs(2, 4, 2, 900, 128, seed=33, with_grad=True)
+@pytest.mark.parametrize("shape,split", [((2, 4, 2, 900, 128), True), ((4, 8, 4, 2048, 128), False)],
+                         ids=["split", "plain"])
+def test_window_deterministic_and_stages(gpu_lib, shape, split):
+    """Bitwise run-to-run determinism; preprocess + grads_window equals
+    bwd_window (bitwise; dK and dV to one bf16 unit in the last place when
+    bwd_window splits the query heads of each K/V head)."""
+    say(f"window determinism and stages {shape}")
+    assert bwd_head_split(gpu_lib, *shape) == split
+    x = make_custom_inputs(*shape, seed=33, with_grad=True)
     a = run(gpu_lib, x, True, 130)
     b = run(gpu_lib, x, True, 130)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
@@ -105,8 +111,12 @@ def test_window_deterministic_and_stages(gpu_lib):
     delta = gpu_lib.bwd_preprocess(o, do)
     g = gpu_lib.bwd_grads(q, k, v, do, lse, delta, causal=True, window=130)
     torch.cuda.synchronize()
-    for u, v in zip(g, a[2]):
-        assert torch.equal(u, v)
+    assert torch.equal(g[0], a[2][0])
+    for u, v in zip(g[1:], a[2][1:]):
+        if split:
+            assert_same_sum_to_bf16_ulp(v, u)
+        else:
+            assert torch.equal(u, v)
 
 
 def test_window_medium_full_check(gpu_lib):
