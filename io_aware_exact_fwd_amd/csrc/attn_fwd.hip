@@ -312,14 +312,9 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  // 8 waves x 32 rows = 256 query rows per workgroup, 128-key tiles (128 KB
-  // of double-buffered LDS: one workgroup per CU), two waves per SIMD.  A
-  // window that covers every key changes nothing and takes the plain kernel.
-  constexpr int BC = 128, NW = 8, WPE = 2;
-  const bool local = a.window >= 0 && a.window < a.N - 1;
+template <int NW>
+hipError_t launch_fwd_nw(const FwdArgs& a, bool local, hipStream_t stream) {
+  constexpr int BC = 128, WPE = 2;
   if (a.d == 128) {
     if (local)
       return a.causal ? launch_fwd_t<128, BC, NW, WPE, true, true>(a, stream)
@@ -332,6 +327,26 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
                     : launch_fwd_t<64, BC, NW, WPE, false, true>(a, stream);
   return a.causal ? launch_fwd_t<64, BC, NW, WPE, true, false>(a, stream)
                   : launch_fwd_t<64, BC, NW, WPE, false, false>(a, stream);
+}
+
+constexpr int kCUs = 256;   // compute units of the chip
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  // 8 waves x 32 rows = 256 query rows per workgroup, 128-key tiles (128 KB
+  // of double-buffered LDS: one workgroup per CU), two waves per SIMD.  A
+  // grid of fewer than 256 such workgroups leaves CUs idle, and one of
+  // exactly 256 under the causal mask (blocks of unequal length) leaves them
+  // unbalanced; there 4-wave workgroups of 128 rows (one wave per SIMD) share
+  // the rows out over twice as many CUs.  A row's arithmetic does not depend
+  // on the workgroup size, so both give bitwise the same O and LSE.  A window
+  // that covers every key changes nothing and takes the plain kernel.
+  const bool local = a.window >= 0 && a.window < a.N - 1;
+  const long long grid8 =
+      packed_grid(a.pack, a.B, a.Hq, 256, (long long)a.B * a.Hq * ((a.N + 255) / 256));
+  const bool small = grid8 < kCUs || (a.causal && !local && grid8 <= kCUs);
+  return small ? launch_fwd_nw<4>(a, local, stream) : launch_fwd_nw<8>(a, local, stream);
 }
 
 }  // namespace attn

@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL_GRAD_REL, TOL_LSE, TOL_O, dev_f64, max_abs, rel_maxnorm, say, to_dev, to_f64
+from gpu_helpers import (TOL_GRAD_REL, TOL_LSE, TOL_O, assert_same_sum_to_bf16_ulp, bwd_head_split, dev_f64,
+                         max_abs, rel_maxnorm, say, to_dev, to_f64)
 from oracle import attention_backward, attention_forward, varlen_backward, varlen_forward
 from synth_inputs import cu_from_lengths, make_custom_inputs, make_inputs
 
@@ -75,7 +76,10 @@ def test_varlen_small(gpu_lib, case, causal):
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
 def test_varlen_equals_per_sequence_calls(gpu_lib, causal):
     """Packing changes nothing: every sequence's rows of O, LSE, dQ, dK, dV are
-    bitwise those of the fixed-length calls on that sequence alone."""
+    bitwise those of the fixed-length calls on that sequence alone -- except
+    that a lone short sequence's backward shares each K/V head's query heads
+    out over several workgroups (packed batches never do), so there its dK and
+    dV agree to one bf16 unit in the last place (fp32 sums in another order)."""
     lengths = [300, 1, 777, 1024, 0, 129]
     say(f"varlen vs per-sequence calls causal={causal}")
     x = pack_draw(lengths, 8, 2, 128, seed=31)
@@ -88,8 +92,14 @@ def test_varlen_equals_per_sequence_calls(gpu_lib, causal):
         so, sl = gpu_lib.fwd(q, k, v, causal=causal)
         sdq, sdk, sdv = gpu_lib.bwd(q, k, v, so, sl, do, causal=causal)
         torch.cuda.synchronize()
-        for packed, alone in ((o, so), (lse, sl), (dq, sdq), (dk, sdk), (dv, sdv)):
+        for packed, alone in ((o, so), (lse, sl), (dq, sdq)):
             assert torch.equal(packed[:, s0:s1], alone[0]), (s0, s1)
+        split = bwd_head_split(gpu_lib, 1, 8, 2, s1 - s0, 128)
+        for packed, alone in ((dk, sdk), (dv, sdv)):
+            if split:
+                assert_same_sum_to_bf16_ulp(alone[0], packed[:, s0:s1])
+            else:
+                assert torch.equal(packed[:, s0:s1], alone[0]), (s0, s1)
 
 
 def _nan_like(shape, dtype):
