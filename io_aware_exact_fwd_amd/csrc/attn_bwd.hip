@@ -575,7 +575,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 // dK/dV units, then its real dQ units, then empty workgroups).  The two
 // halves are independent (both read only the inputs, LSE and D), so dQ blocks
 // fill the CUs that dK/dV blocks release instead of waiting for the whole
-// dK/dV grid to drain.  Both halves use 8 waves.  With S > 1 the dK/dV blocks
+// dK/dV grid to drain.  Both halves use NW waves.  With S > 1 the dK/dV blocks
 // write partial sums to `part` (see dkdv_block) for bwd_dkdv_reduce_kernel.
 template <int D, int NWK, int BC, int NW, int WPE, bool CAUSAL, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
@@ -639,19 +639,30 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// dK/dV: 4 key groups x 2 query halves = 8 waves, 128 keys per workgroup.
-constexpr int kDkdvNWK = 4, kDkdvWPE = 2;
+// Workgroup shapes, per head dimension.  d = 128: dK/dV blocks of 4 key
+// groups x 2 query halves = 8 waves, 128 keys; dQ blocks of 8 waves x 32
+// queries over 128-key tiles (128 KB of double-buffered LDS: one workgroup
+// per CU).  d = 64: half of each -- 2 key groups (64 keys) and 4 dQ waves
+// (128 queries) -- whose LDS (64 KB) lets two workgroups share a CU, so the
+// CU still runs two waves per SIMD over finer blocks (measured 1.00-1.20x
+// the 8-wave launch on every d = 64 shape tried).  A wave's work is the same
+// in both shapes, so the gradients are bitwise equal.
+template <int D>
+struct BwdShape {
+  static constexpr int kNWK = D == 64 ? 2 : 4;    // dK/dV key groups
+  static constexpr int kDqNW = 2 * kNWK;          // dQ waves (= the dK/dV block's waves)
+};
+constexpr int kDkdvWPE = 2;
+constexpr int kDqBC = 128, kDqWPE = 2;
+static_assert(BwdShape<128>::kNWK * 32 == kBwdKeysPerBlock, "the host's split rule counts these blocks");
 // Packed batches keep one workgroup per key block.
 inline int kv_splits_of(const BwdArgs& a) { return a.pack.cu ? 1 : a.kv_splits; }
-static_assert(kDkdvNWK * 32 == kBwdKeysPerBlock, "the host's split rule counts these blocks");
-// dQ: 8 waves x 32 queries, 128-key tiles (128 KB of double-buffered LDS).
-constexpr int kDqBC = 128, kDqNW = 8, kDqWPE = 2;
 
 template <int D, bool CAUSAL, bool LOCAL>
 struct LaunchDkdv {
   static hipError_t run(const BwdArgs& a, hipStream_t stream) {
-    using CK = DkdvCfg<D, kDkdvNWK>;
-    auto kern = bwd_dkdv_kernel<D, kDkdvNWK, kDkdvWPE, CAUSAL, LOCAL>;
+    using CK = DkdvCfg<D, BwdShape<D>::kNWK>;
+    auto kern = bwd_dkdv_kernel<D, BwdShape<D>::kNWK, kDkdvWPE, CAUSAL, LOCAL>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t attr = allow_lds(kern, CK::kLdsBytes, lds_set);
     if (attr != hipSuccess) return attr;
@@ -672,8 +683,8 @@ struct LaunchDkdv {
 template <int D, bool CAUSAL, bool LOCAL>
 struct LaunchDq {
   static hipError_t run(const BwdArgs& a, hipStream_t stream) {
-    using CQ = DqCfg<D, kDqBC, kDqNW>;
-    auto kern = bwd_dq_kernel<D, kDqBC, kDqNW, kDqWPE, CAUSAL, LOCAL>;
+    using CQ = DqCfg<D, kDqBC, BwdShape<D>::kDqNW>;
+    auto kern = bwd_dq_kernel<D, kDqBC, BwdShape<D>::kDqNW, kDqWPE, CAUSAL, LOCAL>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t attr = allow_lds(kern, CQ::kLdsBytes, lds_set);
     if (attr != hipSuccess) return attr;
@@ -694,11 +705,12 @@ struct LaunchDq {
 template <int D, bool CAUSAL, bool LOCAL>
 struct LaunchGrads {
   static hipError_t run(const BwdArgs& a, hipStream_t stream) {
-    using CK = DkdvCfg<D, kDkdvNWK>;
-    using CQ = DqCfg<D, kDqBC, kDqNW>;
+    using CK = DkdvCfg<D, BwdShape<D>::kNWK>;
+    using CQ = DqCfg<D, kDqBC, BwdShape<D>::kDqNW>;
     static_assert(CK::kThreads == CQ::kThreads, "one workgroup size for both halves");
     constexpr int lds = CK::kLdsBytes > CQ::kLdsBytes ? CK::kLdsBytes : CQ::kLdsBytes;
-    auto kern = bwd_grads_kernel<D, kDkdvNWK, kDqBC, kDqNW, kDqWPE, CAUSAL, LOCAL>;
+    auto kern = bwd_grads_kernel<D, BwdShape<D>::kNWK, kDqBC, BwdShape<D>::kDqNW, kDqWPE, CAUSAL,
+                                 LOCAL>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t attr = allow_lds(kern, lds, lds_set);
     if (attr != hipSuccess) return attr;

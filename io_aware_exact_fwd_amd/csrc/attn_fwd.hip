@@ -339,13 +339,18 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   // grid of fewer than 256 such workgroups leaves CUs idle, and one of
   // exactly 256 under the causal mask (blocks of unequal length) leaves them
   // unbalanced; there 4-wave workgroups of 128 rows (one wave per SIMD) share
-  // the rows out over twice as many CUs.  A row's arithmetic does not depend
-  // on the workgroup size, so both give bitwise the same O and LSE.  A window
-  // that covers every key changes nothing and takes the plain kernel.
+  // the rows out over twice as many CUs.  At d = 64 two 4-wave workgroups
+  // (64 KB of LDS each) share a CU, keeping two waves per SIMD, and the finer
+  // blocks also win for short sequences (N <= 2048: 1.07-1.14x at 512-1024
+  // eight-wave blocks) while longer ones tie or lose up to 5 %.  A row's
+  // arithmetic does not depend on the workgroup size, so both give bitwise
+  // the same O and LSE.  A window that covers every key changes nothing and
+  // takes the plain kernel.
   const bool local = a.window >= 0 && a.window < a.N - 1;
   const long long grid8 =
       packed_grid(a.pack, a.B, a.Hq, 256, (long long)a.B * a.Hq * ((a.N + 255) / 256));
-  const bool small = grid8 < kCUs || (a.causal && !local && grid8 <= kCUs);
+  const bool small = grid8 < kCUs || (a.causal && !local && grid8 <= kCUs) ||
+                     (a.d == 64 && a.N <= 2048);
   return small ? launch_fwd_nw<4>(a, local, stream) : launch_fwd_nw<8>(a, local, stream);
 }
 

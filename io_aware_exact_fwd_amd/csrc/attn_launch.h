@@ -96,13 +96,16 @@ struct BwdArgs {
   size_t rows() const { return pack.cu ? (size_t)Hq * pack.T : (size_t)B * Hq * N; }
 };
 
-// Keys per dK/dV workgroup of the backward.
+// Keys per 8-wave dK/dV workgroup of the backward (d = 128; d = 64 runs
+// 4-wave workgroups of half as many keys, two of them per CU).
 constexpr int kBwdKeysPerBlock = 128;
 
 // dK/dV head splits for a fixed-length problem.  Each dK/dV workgroup sums
 // over all G = Hq/Hkv query heads of its K/V head, so with few K/V heads the
-// U = B*Hkv*ceil(N/128) workgroups are too few to fill 256 CUs, or their
-// longest outlast the rest of the launch.  Splitting the heads S ways makes
+// U = B*Hkv*ceil(N/128) workgroups (counted in 128-key blocks, one resident
+// per CU; at d = 64 twice as many 64-key ones, two per CU, the same ratio)
+// are too few to fill 256 CUs, or their longest outlast the rest of the
+// launch.  Splitting the heads S ways makes
 // S*U workgroups of 1/S the work, at the price of 16*d bytes of fp32 partial
 // sums written and read back per key row, K/V head and split.
 //  - Causal, no window: block sizes fall linearly (heaviest first), and the

@@ -173,8 +173,9 @@ def test_bwd_workspace_errors(gpu_lib):
 
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-@pytest.mark.parametrize("shape,split", [((4, 8, 4, 2048, 128), False), ((2, 6, 2, 700, 128), True)],
-                         ids=["plain", "split"])
+@pytest.mark.parametrize("shape,split", [((4, 8, 4, 2048, 128), False), ((2, 6, 2, 700, 128), True),
+                                         ((4, 8, 4, 2048, 64), False)],
+                         ids=["plain", "split", "plain_d64"])
 def test_bwd_stages_equal_bwd(gpu_lib, shape, split, causal):
     """preprocess -> dkdv -> dq and preprocess -> grads give what attn_bwd
     gives: bitwise without the head split; with it, dQ bitwise and dK, dV (one

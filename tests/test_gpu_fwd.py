@@ -202,18 +202,19 @@ def test_fwd_causal_prefix_on_gpu(gpu_lib):
     assert torch.equal(o[:, :, :m], om) and torch.equal(lse[:, :, :m], lm)
 
 
-@pytest.mark.parametrize("causal,window,heads,N", [(True, None, 16, 8192), (False, None, 16, 4096),
-                                                   (True, 1000, 16, 4096), (False, 700, 16, 4096)],
-                         ids=["causal", "full", "causal_w1000", "full_w700"])
-def test_fwd_workgroup_sizes_agree_bitwise(gpu_lib, causal, window, heads, N):
+@pytest.mark.parametrize("causal,window,heads,N,d", [(True, None, 16, 8192, 128), (False, None, 16, 4096, 128),
+                                                     (True, 1000, 16, 4096, 128), (False, 700, 16, 4096, 128),
+                                                     (True, None, 16, 8192, 64)],
+                         ids=["causal", "full", "causal_w1000", "full_w700", "causal_d64"])
+def test_fwd_workgroup_sizes_agree_bitwise(gpu_lib, causal, window, heads, N, d):
     """The launch takes 4-wave workgroups of 128 rows where 8-wave ones of 256
     would leave CUs idle (fewer than 256 of them; exactly 256 under the plain
-    causal mask) and 8-wave ones above that; a row's arithmetic is the same in
-    both.  Heads are independent, so the first half of the heads of each
-    problem (a 4-wave launch) must give bitwise what the whole problem (an
-    8-wave launch) gives for them."""
-    say(f"fwd 4-wave vs 8-wave workgroups causal={causal} window={window}")
-    x = make_custom_inputs(1, heads, heads, N, 128, seed=11)
+    causal mask; at d = 64 also for N <= 2048) and 8-wave ones above that; a
+    row's arithmetic is the same in both.  Heads are independent, so the first
+    half of the heads of each problem (a 4-wave launch) must give bitwise what
+    the whole problem (an 8-wave launch) gives for them."""
+    say(f"fwd 4-wave vs 8-wave workgroups causal={causal} window={window} d={d}")
+    x = make_custom_inputs(1, heads, heads, N, d, seed=11)
     half = {n: np.ascontiguousarray(x[n][:, : heads // 2]) for n in ("q", "k", "v")}
     q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
     o_all, lse_all = gpu_lib.fwd(q, k, v, causal=causal, window=window)
