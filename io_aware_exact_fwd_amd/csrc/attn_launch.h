@@ -105,14 +105,18 @@ constexpr int kBwdKeysPerBlock = 128;
 // U = B*Hkv*ceil(N/128) workgroups (counted in 128-key blocks, one resident
 // per CU; at d = 64 twice as many 64-key ones, two per CU, the same ratio)
 // are too few to fill 256 CUs, or their longest outlast the rest of the
-// launch.  Splitting the heads S ways makes
-// S*U workgroups of 1/S the work, at the price of 16*d bytes of fp32 partial
-// sums written and read back per key row, K/V head and split.
+// launch.  Splitting the heads S ways makes S*U workgroups of 1/S the work,
+// at the price of 16*d bytes of fp32 partial sums written and read back per
+// key row, K/V head and split.
 //  - Causal, no window: block sizes fall linearly (heaviest first), and the
 //    idle tail of the launch is about a fifth of the work times 256 / (S*U).
-//    Against the partials' traffic (both grow as N*d) that is least at
-//    S^2 = 16 G / (B*Hkv), whatever N and d: S is the largest divisor of G
-//    with S^2 * B*Hkv <= 16 G.
+//    With the partials' traffic (both grow as N*d) the cost is, up to one
+//    factor, S + 16 G / (B*Hkv*S) whatever N and d -- least at
+//    S^2 = 16 G / (B*Hkv) -- and S is the divisor of G that minimises it
+//    (the smaller one on a tie).  Splits past 2048 blocks (eight per CU)
+//    are not taken once the chip is full: there the tail is already short
+//    and the partials and per-block set-up cost more than the model's tail
+//    term says (every measured shape's best S kept S*U <= 2048).
 //  - Otherwise every block carries the same work and one full wave of
 //    blocks suffices: the smallest divisor of G with S*U >= 256.
 inline int bwd_kv_splits(int B, int Hq, int Hkv, int N, bool causal, int window) {
@@ -123,11 +127,20 @@ inline int bwd_kv_splits(int B, int Hq, int Hkv, int N, bool causal, int window)
   const bool local = window >= 0 && window < N - 1;
   int S = 1;
   if (causal && !local) {
-    for (int s = 2; s <= G; ++s)
-      if (G % s == 0 && (long long)s * s * bh <= 16LL * G) S = s;
+    // cost(s) * B*Hkv = s*B*Hkv + 16 G / s, compared as s^2*B*Hkv + 16 G over s
+    long long best_num = bh + 16LL * G, best_den = 1;
+    for (int s = 2; s <= G; ++s) {
+      if (G % s != 0 || (units * s > 2048 && units * S >= 256)) continue;
+      const long long num = (long long)s * s * bh + 16LL * G;
+      if (num * best_den < best_num * s) {
+        best_num = num;
+        best_den = s;
+        S = s;
+      }
+    }
   } else {
-    for (S = 1; S < G && units * S < 256;)
-      do ++S; while (G % S != 0);
+    for (int s = 2; s <= G && units * S < 256; ++s)
+      if (G % s == 0) S = s;
   }
   return S;
 }

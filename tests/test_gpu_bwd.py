@@ -130,13 +130,14 @@ def test_bwd_deterministic(gpu_lib, shape):
 # Shapes whose backward shares each K/V head's query heads out over several
 # workgroups (fp32 partial dK/dV in the workspace, added by a reduction):
 # multi-query with many heads, grouped heads with a ragged last key block,
-# d = 64, a batch.
+# d = 64, a batch, a prime group size.
 HEAD_SPLIT = [
     # B, Hq, Hkv, N, d
     (1, 16, 1, 1000, 128),
     (1, 12, 2, 777, 64),
     (2, 8, 2, 300, 128),
     (1, 6, 3, 129, 128),
+    (1, 31, 1, 500, 64),     # prime group: its only split is all 31 heads apart
 ]
 
 
