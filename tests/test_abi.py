@@ -112,6 +112,30 @@ def test_bwd_workspace(L):
     need = L.attn_bwd_workspace_bytes(2, 8, 2, 1000, 128)
     assert need == 2 * 8 * 1000 * 4 + 4 * 2 * (2 * 2 * 1000) * 128 * 4
     assert bwd(L, B=2, Hq=8, Hkv=2, N=1000, d=128, ws_bytes=need - 1) == 4
+
+
+def _splits(L, B, Hq, Hkv, N, d):
+    """The head split count the workspace size encodes (the most either mask takes)."""
+    delta = (B * Hq * N * 4 + 255) // 256 * 256
+    extra = L.attn_bwd_workspace_bytes(B, Hq, Hkv, N, d) - delta
+    per_split = 2 * B * Hkv * N * d * 4
+    assert extra % per_split == 0
+    return max(1, extra // per_split)
+
+
+def test_bwd_head_split_rule(L):
+    """The split count: causal, the divisor S of G = Hq/Hkv minimising
+    S + 16G/(B*Hkv*S), at most 2048 key blocks once 256 are reached; otherwise
+    the fewest splits giving 256 blocks of 128 keys."""
+    assert _splits(L, 1, 32, 1, 8192, 128) == 16      # 16 and 32 tie: the smaller
+    assert _splits(L, 1, 8, 1, 32768, 128) == 8
+    assert _splits(L, 1, 32, 4, 8192, 128) == 4
+    assert _splits(L, 1, 31, 1, 8192, 128) == 31      # prime group: all or nothing
+    assert _splits(L, 1, 64, 8, 16384, 128) == 2      # 4 would pass 2048 blocks
+    assert _splits(L, 4, 32, 8, 4096, 128) == 1       # 1 and 2 tie
+    assert _splits(L, 1, 8, 8, 32768, 128) == 1       # no grouping
+    assert _splits(L, 1, 32, 1, 8192, 64) == 16       # the same at d = 64
+    assert _splits(L, 2, 16, 2, 4096, 128) == 4       # causal 4, full 2: the larger
     assert L.attn_bwd_workspace_bytes(1, 3, 2, 10, 64) == 0      # invalid problem -> 0
 
 
