@@ -642,7 +642,8 @@ hipError_t launch_pre_t(const BwdArgs& a, hipStream_t stream) {
 // Workgroup shapes, per head dimension.  d = 128: dK/dV blocks of 4 key
 // groups x 2 query halves = 8 waves, 128 keys; dQ blocks of 8 waves x 32
 // queries over 128-key tiles (128 KB of double-buffered LDS: one workgroup
-// per CU).  d = 64: half of each -- 2 key groups (64 keys) and 4 dQ waves
+// per CU); the d = 64 shape below on grids too short to fill the chip
+// (LaunchGrads).  d = 64: half of each -- 2 key groups (64 keys) and 4 dQ waves
 // (128 queries) -- whose LDS (64 KB) lets two workgroups share a CU, so the
 // CU still runs two waves per SIMD over finer blocks (measured 1.00-1.20x
 // the 8-wave launch on every d = 64 shape tried).  A wave's work is the same
@@ -654,6 +655,7 @@ struct BwdShape {
 };
 constexpr int kDkdvWPE = 2;
 constexpr int kDqBC = 128, kDqWPE = 2;
+constexpr int kBwdCUs = 256;   // compute units of the chip
 static_assert(BwdShape<128>::kNWK * 32 == kBwdKeysPerBlock, "the host's split rule counts these blocks");
 // Packed batches keep one workgroup per key block.
 inline int kv_splits_of(const BwdArgs& a) { return a.pack.cu ? 1 : a.kv_splits; }
@@ -704,13 +706,14 @@ struct LaunchDq {
 
 template <int D, bool CAUSAL, bool LOCAL>
 struct LaunchGrads {
-  static hipError_t run(const BwdArgs& a, hipStream_t stream) {
-    using CK = DkdvCfg<D, BwdShape<D>::kNWK>;
-    using CQ = DqCfg<D, kDqBC, BwdShape<D>::kDqNW>;
+  // One launch with NWK key groups per dK/dV block and 2*NWK dQ waves.
+  template <int NWK>
+  static hipError_t run_shape(const BwdArgs& a, hipStream_t stream) {
+    using CK = DkdvCfg<D, NWK>;
+    using CQ = DqCfg<D, kDqBC, 2 * NWK>;
     static_assert(CK::kThreads == CQ::kThreads, "one workgroup size for both halves");
     constexpr int lds = CK::kLdsBytes > CQ::kLdsBytes ? CK::kLdsBytes : CQ::kLdsBytes;
-    auto kern = bwd_grads_kernel<D, BwdShape<D>::kNWK, kDqBC, BwdShape<D>::kDqNW, kDqWPE, CAUSAL,
-                                 LOCAL>;
+    auto kern = bwd_grads_kernel<D, NWK, kDqBC, 2 * NWK, kDqWPE, CAUSAL, LOCAL>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t attr = allow_lds(kern, lds, lds_set);
     if (attr != hipSuccess) return attr;
@@ -730,6 +733,24 @@ struct LaunchGrads {
                        n_qb, a.scale, a.scale * kLog2e, xcd_remap(BHkv * S, a.pack),
                        xcd_remap(BH, a.pack), a.window, a.pack, S, S > 1 ? a.part : nullptr);
     return hipGetLastError();
+  }
+
+  // d = 128 takes 4-wave blocks too when the 8-wave grid would not fill the
+  // chip: at one 4-wave workgroup per CU (128 KB of LDS) twice as many CUs
+  // then work (1.15-1.28x measured at 96-192 eight-wave blocks, 15-23 %
+  // slower from 384 up); the gradients are bitwise the same.
+  static hipError_t run(const BwdArgs& a, hipStream_t stream) {
+    if (D == 128) {
+      using CK = DkdvCfg<D, BwdShape<D>::kNWK>;
+      using CQ = DqCfg<D, kDqBC, BwdShape<D>::kDqNW>;
+      const long long n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
+      const long long n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
+      const long long grid8 =
+          packed_grid(a.pack, a.B, a.Hkv, CK::kBKV, (long long)a.B * a.Hkv * n_kb * kv_splits_of(a)) +
+          packed_grid(a.pack, a.B, a.Hq, CQ::kBQ, (long long)a.B * a.Hq * n_qb);
+      if (grid8 < kBwdCUs) return run_shape<BwdShape<64>::kNWK>(a, stream);
+    }
+    return run_shape<BwdShape<D>::kNWK>(a, stream);
   }
 };
 

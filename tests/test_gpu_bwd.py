@@ -150,6 +150,29 @@ def test_bwd_head_split(gpu_lib, shape, causal):
     check_grads(gpu_lib, x, causal, label=f"split {shape}")
 
 
+@pytest.mark.parametrize("window", [None, 500], ids=["causal", "causal_w500"])
+def test_bwd_workgroup_sizes_agree_bitwise(gpu_lib, window):
+    """At d = 128 the gradient launch takes 4-wave blocks (64 keys, 128
+    queries) when its 8-wave grid has fewer than 256 blocks, 8-wave blocks
+    above; a wave's work is the same in both.  With one query head per K/V
+    head the heads are independent, so the first half of the heads (192
+    eight-wave blocks: a 4-wave launch) must give bitwise the gradients the
+    whole problem (384: an 8-wave launch) gives for them."""
+    say(f"bwd 4-wave vs 8-wave workgroups window={window}")
+    x = make_custom_inputs(1, 8, 8, 4096, 128, seed=18, with_grad=True)
+    half = {n: np.ascontiguousarray(x[n][:, :4]) for n in ("q", "k", "v", "do")}
+
+    def grads(inp):
+        q, k, v, do = (to_dev(inp[n]) for n in ("q", "k", "v", "do"))
+        o, lse = gpu_lib.fwd(q, k, v, causal=True, window=window)
+        return gpu_lib.bwd(q, k, v, o, lse, do, causal=True, window=window)
+
+    full_g, half_g = grads(x), grads(half)
+    torch.cuda.synchronize()
+    for a, b in zip(full_g, half_g):
+        assert torch.equal(a[:, :4], b)
+
+
 @pytest.mark.timeout(600)
 def test_bwd_head_split_mqa_4k(gpu_lib):
     """Multi-query at its working size: 32 query heads over one K/V head,
