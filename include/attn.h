@@ -250,7 +250,16 @@ int attn_fwd_decode_static(const void* q, const void* k, const void* v, void* o,
  *   max_seqlen      the longest sequence (bounds the grid): 1 <= max_seqlen <= total
  *   window < 0: none; >= 0: as attn_fwd_window, within each sequence
  *   workspace       attn_bwd_varlen: >= attn_bwd_varlen_workspace_bytes(Hq, total, d)
- *                   bytes (fp32 D per packed query row); contents on exit unspecified
+ *                   bytes (fp32 D per packed query row); contents on exit unspecified.
+ *                   With at least attn_bwd_varlen_split_workspace_bytes(B, total,
+ *                   max_seqlen, Hq, Hkv, d) bytes, attn_bwd_varlen may share the
+ *                   Hq/Hkv query heads of each K/V head out over several workgroups
+ *                   (as attn_bwd does, with the fp32 partial dK/dV after D in the
+ *                   workspace) when the packed dK/dV grid is too short for the chip;
+ *                   dQ is the same either way and dK, dV then differ from the
+ *                   smaller workspace's by one bf16 unit in the last place at most.
+ *                   Either way the result is deterministic for a given workspace
+ *                   size class (below or at least the split size).
  *
  * The boundaries live on the device and are not read by the host; with up to
  * 512 sequences each workgroup finds its own (sequence, head, block) among the
@@ -267,6 +276,13 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     const int* cu_seqlens, int B, int total, int max_seqlen, int Hq, int Hkv,
                     int d, int causal, int window, float scale, void* stream);
 size_t attn_bwd_varlen_workspace_bytes(int Hq, int total, int d);
+/* Workspace bytes that let attn_bwd_varlen split query heads over workgroups
+ * (see `workspace` above): D rounded up to 256 bytes, plus S*2*Hkv*total*d*4
+ * for the split count S the shape takes (the larger of the causal and full
+ * masks' counts; no extra when S = 1).  Returns 0 for invalid arguments
+ * (the rules of attn_bwd_varlen). */
+size_t attn_bwd_varlen_split_workspace_bytes(int B, int total, int max_seqlen, int Hq, int Hkv,
+                                             int d);
 int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
                     const int* cu_seqlens, void* workspace, size_t workspace_bytes,

@@ -22,6 +22,7 @@ import torch  # loads the HIP runtime that libattn.so then binds to
 __all__ = [
     "AttnError", "fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_grads", "fwd_decode",
     "decode_workspace_bytes", "fwd_decode_static", "DECODE_STATIC_SCRATCH_BYTES", "fwd_varlen", "bwd_varlen", "bwd_varlen_workspace_bytes",
+    "bwd_varlen_split_workspace_bytes",
     "bwd_grads_varlen", "fwd_fp8", "attention", "attention_varlen",
     "bwd_workspace_bytes",
     "device_check", "strerror", "lib", "LIB_PATH", "EXPORTED",
@@ -33,6 +34,7 @@ EXPORTED = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_prepro
             "attn_device_check", "attn_fwd_window", "attn_bwd_window", "attn_bwd_grads_window",
             "attn_fwd_decode", "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
             "attn_bwd_varlen", "attn_bwd_varlen_workspace_bytes", "attn_bwd_grads_varlen",
+            "attn_bwd_varlen_split_workspace_bytes",
             "attn_fwd_fp8", "attn_fwd_decode_static")
 
 ATTN_OK = 0
@@ -95,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_fp8.restype = i
     L.attn_bwd_varlen_workspace_bytes.argtypes = [i, i, i]
     L.attn_bwd_varlen_workspace_bytes.restype = sz
+    L.attn_bwd_varlen_split_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_bwd_varlen_split_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_strerror.argtypes = [i]
@@ -407,6 +411,12 @@ def bwd_varlen_workspace_bytes(Hq: int, total: int, d: int) -> int:
     return int(lib().attn_bwd_varlen_workspace_bytes(Hq, total, d))
 
 
+def bwd_varlen_split_workspace_bytes(B: int, total: int, max_seqlen: int, Hq: int, Hkv: int,
+                                     d: int) -> int:
+    """Workspace bytes with which bwd_varlen may split query heads over workgroups."""
+    return int(lib().attn_bwd_varlen_split_workspace_bytes(B, total, max_seqlen, Hq, Hkv, d))
+
+
 def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens,
                max_seqlen: Optional[int] = None, causal: bool = True,
                scale: Optional[float] = None, window: Optional[int] = None,
@@ -459,8 +469,8 @@ def bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
     _check_bf16("dk", dk, (Hkv, T, d))
     _check_bf16("dv", dv, (Hkv, T, d))
     if workspace is None:
-        workspace = torch.empty(max(bwd_varlen_workspace_bytes(Hq, T, d), 16), dtype=torch.uint8,
-                                device=q.device)
+        need = bwd_varlen_split_workspace_bytes(B, T, max_seqlen, Hq, Hkv, d)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace)
     tau = 1.0 / math.sqrt(d) if scale is None else float(scale)
     rc = lib().attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),

@@ -334,6 +334,13 @@ ATTN_EXPORT size_t attn_bwd_varlen_workspace_bytes(int Hq, int total, int d) {
   return (size_t)Hq * total * sizeof(float);
 }
 
+ATTN_EXPORT size_t attn_bwd_varlen_split_workspace_bytes(int B, int total, int max_seqlen, int Hq,
+                                                         int Hkv, int d) {
+  if (check_varlen(B, total, max_seqlen, Hq, Hkv, d)) return 0;
+  return attn::bwd_varlen_workspace_bytes(
+      total, Hq, Hkv, d, attn::bwd_kv_splits_packed_max(total, max_seqlen, Hq, Hkv));
+}
+
 ATTN_EXPORT int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                 const int* cu_seqlens, void* workspace, size_t workspace_bytes,
@@ -353,6 +360,12 @@ ATTN_EXPORT int attn_bwd_varlen(const void* q, const void* k, const void* v, con
   attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace,
                   B, Hq, Hkv, max_seqlen, d, causal != 0, scale, window < 0 ? -1 : window};
   a.pack = attn::Packing{cu_seqlens, total};
+  // the head split, when the workspace has room for its partials after D
+  const int S = attn::bwd_kv_splits_packed(total, max_seqlen, Hq, Hkv, causal != 0, a.window);
+  if (S > 1 && workspace_bytes >= attn::bwd_varlen_workspace_bytes(total, Hq, Hkv, d, S)) {
+    a.kv_splits = S;
+    a.part = (float*)((char*)workspace + attn::bwd_delta_bytes(1, Hq, total));
+  }
   hipError_t e = attn::launch_bwd(a, (hipStream_t)stream);
   return e == hipSuccess ? ATTN_OK : hip_fail(e, "attn_bwd_varlen launch");
 }

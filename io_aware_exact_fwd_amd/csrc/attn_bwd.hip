@@ -83,10 +83,9 @@ struct DkdvCfg {
 };
 
 // One dK/dV workgroup: w is its index in the dK/dV grid, smem its LDS.  With
-// LOCAL, query i sees key j only when |i - j| <= window.  With S > 1 (fixed
-// length only) the G query heads of each K/V head are shared out over S
-// workgroups of G/S heads each, which write fp32 partial sums to `part`
-// instead of dK and dV.
+// LOCAL, query i sees key j only when |i - j| <= window.  With S > 1 the G
+// query heads of each K/V head are shared out over S workgroups of G/S heads
+// each, which write fp32 partial sums to `part` instead of dK and dV.
 template <int D, int NWK, bool CAUSAL, bool LOCAL>
 __device__ __forceinline__ void dkdv_block(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -112,10 +111,13 @@ __device__ __forceinline__ void dkdv_block(
   int b, hk, kb, split = 0;
   if (pk.cu && BHkv / Hkv <= kMaxPackedSeqs) {
     // packed: real key blocks only, heaviest (most query tiles after them) first
+    // (K/V head, split) pairs take the place of heads
     PackedUnits pu;
     pu.init(pk, BHkv / Hkv, Nmax, C::kBKV);
-    int level;
-    if (!pu.unit(w, Hkv, b, hk, level)) return;
+    int level, hks;
+    if (!pu.unit(w, Hkv * S, b, hks, level)) return;
+    hk = hks / S;
+    split = hks - hk * S;
     const int len = seq_span(pk, Nmax, b).len;
     kb = (len + C::kBKV - 1) / C::kBKV - 1 - level;
   } else {
@@ -325,7 +327,7 @@ __device__ __forceinline__ void dkdv_block(
   const int key = kw0 + l32;
   if (key < N && part) {
     // this split's fp32 sums, dK still unscaled
-    const size_t plane = (size_t)BHkv * Nmax * D;
+    const size_t plane = pk.cu ? (size_t)Hkv * pk.T * D : (size_t)BHkv * Nmax * D;
     float* pkr = part + 2 * split * plane + kv_off + (size_t)key * D;
     float* pvr = pkr + plane;
 #pragma unroll
@@ -594,7 +596,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
     // rest of the grid (sized for the longest sequence) is empty
     PackedUnits pu;
     pu.init(pk, BHkv / Hkv, N, DkdvCfg<D, NWK>::kBKV);
-    split = (int)pu.at_or_above(0, Hkv);
+    split = (int)pu.at_or_above(0, Hkv * S);
   }
   if (w < split)
     dkdv_block<D, NWK, CAUSAL, LOCAL>(Q, K, V, dO, LSE, Dl, dK, dV, N, BHkv, Hq, Hkv, G, scale,
@@ -657,8 +659,7 @@ constexpr int kDkdvWPE = 2;
 constexpr int kDqBC = 128, kDqWPE = 2;
 constexpr int kBwdCUs = 256;   // compute units of the chip
 static_assert(BwdShape<128>::kNWK * 32 == kBwdKeysPerBlock, "the host's split rule counts these blocks");
-// Packed batches keep one workgroup per key block.
-inline int kv_splits_of(const BwdArgs& a) { return a.pack.cu ? 1 : a.kv_splits; }
+inline int kv_splits_of(const BwdArgs& a) { return a.kv_splits; }
 
 template <int D, bool CAUSAL, bool LOCAL>
 struct LaunchDkdv {
@@ -722,7 +723,7 @@ struct LaunchGrads {
     const int n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
     const int S = kv_splits_of(a);
     const long long n_dkdv = (long long)BHkv * n_kb * S;
-    const long long grid = packed_grid(a.pack, a.B, a.Hkv, CK::kBKV, n_dkdv) +
+    const long long grid = packed_grid(a.pack, a.B, a.Hkv * S, CK::kBKV, n_dkdv) +
                            packed_grid(a.pack, a.B, a.Hq, CQ::kBQ, (long long)BH * n_qb);
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (grid == 0) return hipSuccess;
@@ -745,8 +746,9 @@ struct LaunchGrads {
       using CQ = DqCfg<D, kDqBC, BwdShape<D>::kDqNW>;
       const long long n_kb = (a.N + CK::kBKV - 1) / CK::kBKV;
       const long long n_qb = (a.N + CQ::kBQ - 1) / CQ::kBQ;
+      const int S = kv_splits_of(a);
       const long long grid8 =
-          packed_grid(a.pack, a.B, a.Hkv, CK::kBKV, (long long)a.B * a.Hkv * n_kb * kv_splits_of(a)) +
+          packed_grid(a.pack, a.B, a.Hkv * S, CK::kBKV, (long long)a.B * a.Hkv * n_kb * S) +
           packed_grid(a.pack, a.B, a.Hq, CQ::kBQ, (long long)a.B * a.Hq * n_qb);
       if (grid8 < kBwdCUs) return run_shape<BwdShape<64>::kNWK>(a, stream);
     }
@@ -774,7 +776,8 @@ hipError_t launch_bwd_grads(const BwdArgs& a, hipStream_t stream) {
   if (S < 1 || (a.Hq / a.Hkv) % S != 0 || (S > 1 && !a.part)) return hipErrorInvalidValue;
   hipError_t e = dispatch<LaunchGrads>(a, stream);
   if (e != hipSuccess || S == 1) return e;
-  const size_t n4 = (size_t)a.B * a.Hkv * a.N * a.d / 4;
+  // one plane of dK (or dV): B*Hkv*N rows, packed Hkv*T
+  const size_t n4 = (a.pack.cu ? (size_t)a.Hkv * a.pack.T : (size_t)a.B * a.Hkv * a.N) * a.d / 4;
   hipLaunchKernelGGL(bwd_dkdv_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0,
                      stream, a.part, (uint16_t*)a.dk, (uint16_t*)a.dv, n4, S, a.scale);
   return hipGetLastError();

@@ -88,8 +88,9 @@ struct BwdArgs {
   Packing pack;
   // dK/dV head split: the Hq/Hkv query heads of a K/V head are shared out
   // over kv_splits workgroups per key block, each writing fp32 partial sums
-  // [kv_splits, 2 (dK unscaled, dV), B*Hkv*N, d] to `part`; a reduction adds
-  // them in split order.  1 = one workgroup sums all heads and writes bf16.
+  // [kv_splits, 2 (dK unscaled, dV), B*Hkv*N (packed: Hkv*T), d] to `part`;
+  // a reduction adds them in split order.  1 = one workgroup sums all heads
+  // and writes bf16.
   int kv_splits = 1;
   float* part = nullptr;
   // query rows over all heads: B*Hq*N, or Hq*T when packed
@@ -119,14 +120,12 @@ constexpr int kBwdKeysPerBlock = 128;
 //    term says (every measured shape's best S kept S*U <= 2048).
 //  - Otherwise every block carries the same work and one full wave of
 //    blocks suffices: the smallest divisor of G with S*U >= 256.
-inline int bwd_kv_splits(int B, int Hq, int Hkv, int N, bool causal, int window) {
-  const int G = Hq / Hkv;
+// The rule over bh = B*Hkv (independent K/V heads of the longest length) and
+// U dK/dV blocks of 128 keys.
+inline int bwd_kv_splits_rule(int G, long long bh, long long units, bool causal_plain) {
   if (G < 2) return 1;
-  const long long bh = (long long)B * Hkv;
-  const long long units = bh * ((N + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock);
-  const bool local = window >= 0 && window < N - 1;
   int S = 1;
-  if (causal && !local) {
+  if (causal_plain) {
     // cost(s) * B*Hkv = s*B*Hkv + 16 G / s, compared as s^2*B*Hkv + 16 G over s
     long long best_num = bh + 16LL * G, best_den = 1;
     for (int s = 2; s <= G; ++s) {
@@ -143,6 +142,26 @@ inline int bwd_kv_splits(int B, int Hq, int Hkv, int N, bool causal, int window)
       if (G % s == 0) S = s;
   }
   return S;
+}
+
+inline int bwd_kv_splits(int B, int Hq, int Hkv, int N, bool causal, int window) {
+  const long long bh = (long long)B * Hkv;
+  const long long units = bh * ((N + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock);
+  const bool local = window >= 0 && window < N - 1;
+  return bwd_kv_splits_rule(Hq / Hkv, bh, units, causal && !local);
+}
+
+// A packed batch of `total` rows whose longest sequence has max_seqlen: about
+// Hkv*total/128 dK/dV blocks (one more per sequence at most, for ragged
+// ends), and the causal model takes it as ceil(total / max_seqlen)
+// sequences of the longest length.
+inline int bwd_kv_splits_packed(int total, int max_seqlen, int Hq, int Hkv, bool causal,
+                                int window) {
+  if (total <= 0 || max_seqlen <= 0) return 1;
+  const long long seqs = ((long long)total + max_seqlen - 1) / max_seqlen;
+  const long long units = (long long)Hkv * (((long long)total + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock);
+  const bool local = window >= 0 && window < max_seqlen - 1;
+  return bwd_kv_splits_rule(Hq / Hkv, seqs * Hkv, units, causal && !local);
 }
 
 // The most splits any mask takes for this shape: the workspace holds that many.
@@ -164,6 +183,18 @@ inline size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   const int S = bwd_kv_splits_max(B, Hq, Hkv, N);
   const size_t part = S > 1 ? (size_t)S * 2 * B * Hkv * N * d * sizeof(float) : 0;
   return bwd_delta_bytes(B, Hq, N) + part;
+}
+
+// A packed batch: D over Hq*total rows (rounded to 256 bytes), and the
+// partials of S splits over Hkv*total key rows.
+inline size_t bwd_varlen_workspace_bytes(int total, int Hq, int Hkv, int d, int S) {
+  const size_t part = S > 1 ? (size_t)S * 2 * Hkv * total * d * sizeof(float) : 0;
+  return bwd_delta_bytes(1, Hq, total) + part;
+}
+inline int bwd_kv_splits_packed_max(int total, int max_seqlen, int Hq, int Hkv) {
+  const int a = bwd_kv_splits_packed(total, max_seqlen, Hq, Hkv, true, -1);
+  const int b = bwd_kv_splits_packed(total, max_seqlen, Hq, Hkv, false, -1);
+  return a > b ? a : b;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
@@ -218,9 +249,9 @@ constexpr size_t kDecodeStaticScratchBytes = size_t{32} << 20;
 hipError_t decode_static_scratch(float** out);
 // The backward's stages.  Each reads the BwdArgs fields it needs (delta must
 // be set for all of them).  launch_bwd_grads runs dK/dV and dQ in one launch,
-// followed by the reduction of the partial sums when kv_splits > 1 (fixed
-// length only; launch_bwd_dkdv ignores kv_splits); launch_bwd is
-// launch_bwd_pre followed by launch_bwd_grads.
+// followed by the reduction of the partial sums when kv_splits > 1
+// (launch_bwd_dkdv ignores kv_splits); launch_bwd is launch_bwd_pre followed
+// by launch_bwd_grads.
 hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);

@@ -98,3 +98,10 @@ def assert_same_sum_to_bf16_ulp(a: torch.Tensor, b: torch.Tensor) -> None:
     x, y = a.float(), b.float()
     bound = 2.0 ** -7 * torch.maximum(x.abs(), y.abs()) + 1e-4 * float(y.abs().max())
     assert bool(((x - y).abs() <= bound).all()), float(((x - y).abs() - bound).max())
+
+
+def varlen_head_split(attn, B: int, T: int, max_seqlen: int, Hq: int, Hkv: int, d: int) -> bool:
+    """Whether bwd_varlen, given its default (split-size) workspace, shares each
+    K/V head's query heads out over several workgroups for some mask."""
+    delta = (Hq * T * 4 + 255) // 256 * 256
+    return attn.bwd_varlen_split_workspace_bytes(B, T, max_seqlen, Hq, Hkv, d) > delta

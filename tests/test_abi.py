@@ -38,6 +38,7 @@ def test_header_declares_the_boundary():
                                            "attn_fwd_decode_workspace_bytes", "attn_fwd_varlen",
                                            "attn_bwd_varlen", "attn_bwd_grads_varlen", "attn_fwd_fp8",
                                            "attn_bwd_varlen_workspace_bytes",
+                                           "attn_bwd_varlen_split_workspace_bytes",
                                            "attn_fwd_decode_static"])
 
 
@@ -254,6 +255,15 @@ def test_varlen_validation_and_workspace(L):
     assert L.attn_bwd_varlen_workspace_bytes(8, 1000, 128) == 8 * 1000 * 4
     assert L.attn_bwd_varlen_workspace_bytes(8, 1000, 96) == 0
     assert L.attn_bwd_varlen_workspace_bytes(0, 1000, 128) == 0
+    # the size that allows the head split: D rounded to 256 bytes, then S
+    # partial dK/dV planes [2, Hkv, total, d] fp32 -- 32 heads over 1 K/V head,
+    # 8192 packed rows in sequences of at most 4096 (two at that length): 16
+    sp = L.attn_bwd_varlen_split_workspace_bytes
+    assert sp(4, 8192, 4096, 32, 1, 128) == 32 * 8192 * 4 + 16 * 2 * 8192 * 128 * 4
+    assert sp(4, 8192, 4096, 8, 8, 128) == 8 * 8192 * 4          # no grouping: no split
+    assert sp(2, 1000, 600, 3, 3, 64) == (3 * 1000 * 4 + 255) // 256 * 256
+    assert sp(2, 100, 200, 4, 2, 64) == 0                         # max_seqlen > total
+    assert sp(2, 100, 60, 4, 2, 96) == 0                          # d
     f = L.attn_fwd_varlen
     #         q  k  v  o  lse cu   B  T    max Hq Hkv d  causal win scale
     assert f(A, A, A, A, A, A, 0, 100, 60, 4, 2, 64, 1, -1, 0.1, None) == 2        # B = 0

@@ -147,10 +147,13 @@ def test_decode_writes_only_its_outputs(gpu_lib, splits):
     assert max_abs(dev_f64(o), ro) <= TOL_O and max_abs(dev_f64(lse), rl) <= TOL_LSE
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["min_workspace", "split_workspace"])
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-def test_packed_batches_write_only_their_outputs(gpu_lib, causal):
+def test_packed_batches_write_only_their_outputs(gpu_lib, causal, split):
     """A packed batch with a one-token sequence, an empty one and ragged tails:
-    O, LSE, D, dQ, dK, dV and the workspace guarded; every packed row written."""
+    O, LSE, D, dQ, dK, dV and the workspace guarded; every packed row written.
+    With the split-size workspace the backward also writes its partial sums
+    there (two K/V heads of two query heads each, split two ways)."""
     lengths, Hq, Hkv, d = [1, 0, 129, 1, 270, 0, 64], 4, 2, 128
     T = sum(lengths)
     say(f"canary packed {lengths} causal={causal}")
@@ -166,7 +169,8 @@ def test_packed_batches_write_only_their_outputs(gpu_lib, causal):
     dq = g.tensor((Hq, T, d), torch.bfloat16)
     dk = g.tensor((Hkv, T, d), torch.bfloat16)
     dv = g.tensor((Hkv, T, d), torch.bfloat16)
-    ws = g.workspace(gpu_lib.bwd_varlen_workspace_bytes(Hq, T, d))
+    ws = g.workspace(gpu_lib.bwd_varlen_split_workspace_bytes(len(lengths), T, max(lengths), Hq, Hkv, d)
+                     if split else gpu_lib.bwd_varlen_workspace_bytes(Hq, T, d))
     gpu_lib.bwd_varlen(q, k, v, o, lse, do, cu, max(lengths), causal=causal, dq=dq, dk=dk, dv=dv,
                        workspace=ws)
     g.check("packed fwd + bwd")

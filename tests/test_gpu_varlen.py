@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from gpu_helpers import (TOL_GRAD_REL, TOL_LSE, TOL_O, assert_same_sum_to_bf16_ulp, bwd_head_split, dev_f64,
-                         max_abs, rel_maxnorm, say, to_dev, to_f64)
+                         max_abs, rel_maxnorm, say, to_dev, to_f64, varlen_head_split)
 from oracle import attention_backward, attention_forward, varlen_backward, varlen_forward
 from synth_inputs import cu_from_lengths, make_custom_inputs, make_inputs
 
@@ -77,14 +77,15 @@ def test_varlen_small(gpu_lib, case, causal):
 def test_varlen_equals_per_sequence_calls(gpu_lib, causal):
     """Packing changes nothing: every sequence's rows of O, LSE, dQ, dK, dV are
     bitwise those of the fixed-length calls on that sequence alone -- except
-    that a lone short sequence's backward shares each K/V head's query heads
-    out over several workgroups (packed batches never do), so there its dK and
-    dV agree to one bf16 unit in the last place (fp32 sums in another order)."""
+    that where either backward shares each K/V head's query heads out over
+    several workgroups (each picks its own split count), dK and dV agree to
+    one bf16 unit in the last place (fp32 sums in another order)."""
     lengths = [300, 1, 777, 1024, 0, 129]
     say(f"varlen vs per-sequence calls causal={causal}")
     x = pack_draw(lengths, 8, 2, 128, seed=31)
     o, lse, dq, dk, dv = run(gpu_lib, x, causal)
     cu = x["cu_seqlens"].tolist()
+    packed_split = varlen_head_split(gpu_lib, len(lengths), sum(lengths), max(lengths), 8, 2, 128)
     for s0, s1 in zip(cu, cu[1:]):
         if s1 == s0:
             continue
@@ -94,7 +95,7 @@ def test_varlen_equals_per_sequence_calls(gpu_lib, causal):
         torch.cuda.synchronize()
         for packed, alone in ((o, so), (lse, sl), (dq, sdq)):
             assert torch.equal(packed[:, s0:s1], alone[0]), (s0, s1)
-        split = bwd_head_split(gpu_lib, 1, 8, 2, s1 - s0, 128)
+        split = packed_split or bwd_head_split(gpu_lib, 1, 8, 2, s1 - s0, 128)
         for packed, alone in ((dk, sdk), (dv, sdv)):
             if split:
                 assert_same_sum_to_bf16_ulp(alone[0], packed[:, s0:s1])
@@ -158,20 +159,71 @@ def test_varlen_many_sequences(gpu_lib, case, causal):
 
 def test_varlen_device_table_and_stages(gpu_lib):
     """A device-resident table with max_seqlen given is used unread by the
-    host; the split pre-pass + gradient stage equals bwd_varlen bitwise."""
+    host; the split pre-pass + gradient stage equals bwd_varlen (bitwise with
+    the smallest workspace; with the default one bwd_varlen splits this
+    batch's query heads, and dK, dV then agree to one bf16 ulp)."""
     lengths = [400, 1500, 3]
     say("varlen device table, stages")
     x = pack_draw(lengths, 4, 2, 128, seed=41)
+    assert varlen_head_split(gpu_lib, 3, sum(lengths), 1500, 4, 2, 128)
     o, lse, dq, dk, dv = run(gpu_lib, x, True)
     q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
     cu_dev = torch.from_numpy(x["cu_seqlens"]).cuda()
     o2, lse2 = gpu_lib.fwd_varlen(q, k, v, cu_dev, max_seqlen=1500, causal=True)
     delta = gpu_lib.bwd_preprocess(o2[None], do[None])[0]
     g = gpu_lib.bwd_grads_varlen(q, k, v, do, lse2, delta, cu_dev, max_seqlen=1500, causal=True)
+    small = torch.empty(gpu_lib.bwd_varlen_workspace_bytes(4, sum(lengths), 128), dtype=torch.uint8,
+                        device="cuda")
+    g1 = gpu_lib.bwd_varlen(q, k, v, o2, lse2, do, cu_dev, max_seqlen=1500, causal=True, workspace=small)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
-    for a, b in zip((dq, dk, dv), g):
+    for a, b in zip(g1, g):
         assert torch.equal(a, b)
+    assert torch.equal(dq, g[0])
+    assert_same_sum_to_bf16_ulp(dk, g[1])
+    assert_same_sum_to_bf16_ulp(dv, g[2])
+
+
+# Packed batches whose dK/dV grid is short: few K/V heads over a few thousand
+# packed rows.  With the default workspace bwd_varlen splits each K/V head's
+# query heads over several workgroups (real-block order; the last case has
+# more than 512 sequences and takes the plain grid).
+PACKED_SPLIT = [
+    # lengths, Hq, Hkv, d
+    ([700, 1, 1500, 0, 333], 16, 1, 128),
+    ([129, 64, 1000, 7], 12, 2, 64),
+    ([3] * 520 + [250], 4, 1, 64),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("case", PACKED_SPLIT, ids=["mqa16", "gqa12_2_d64", "b521_plain_grid"])
+def test_varlen_head_split(gpu_lib, case, causal):
+    """Oracle parity with the split; against the smallest workspace (no
+    split): dQ bitwise, dK and dV to one bf16 ulp; run to run bitwise."""
+    lengths, Hq, Hkv, d = case
+    T = sum(lengths)
+    say(f"varlen head split B={len(lengths)} T={T} Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    assert varlen_head_split(gpu_lib, len(lengths), T, max(lengths), Hq, Hkv, d)
+    x = pack_draw(lengths, Hq, Hkv, d, seed=61 + Hq, in_scale=0.5)
+    o, lse, dq, dk, dv = run(gpu_lib, x, causal)
+    _, _, dq2, dk2, dv2 = run(gpu_lib, x, causal)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    cu = torch.from_numpy(x["cu_seqlens"])
+    small = torch.empty(gpu_lib.bwd_varlen_workspace_bytes(Hq, T, d), dtype=torch.uint8, device="cuda")
+    g1 = gpu_lib.bwd_varlen(q, k, v, o, lse, do, cu, causal=causal, workspace=small)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.equal(dq, g1[0])
+    assert_same_sum_to_bf16_ulp(dk, g1[1])
+    assert_same_sum_to_bf16_ulp(dv, g1[2])
+    f = {n: to_f64(x[n]) for n in ("q", "k", "v", "do")}
+    cul = x["cu_seqlens"].tolist()
+    rdq, rdk, rdv = varlen_backward(f["q"], f["k"], f["v"], f["do"], cul, causal)
+    floor = 1e-3 * max(float(t.abs().max()) for t in (rdq, rdk, rdv))
+    errs = [rel_maxnorm(dev_f64(a), r, floor) for a, r in ((dq, rdq), (dk, rdk), (dv, rdv))]
+    print(f"packed split {case[1:]} causal={causal}: dQ/dK/dV = {errs}")
+    assert max(errs) <= TOL_GRAD_REL, errs
 
 
 def test_varlen_empty_batch_and_host_checks(gpu_lib):
